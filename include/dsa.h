@@ -1,0 +1,186 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The path has three stages (the two-stage data flow of the charlestar page
+ * "DeepSeek V3.2 稀疏注意力", section "DSA 的两段式数据流"):
+ *
+ *   1. Lightning Indexer score ("详解DSA", Eq.(1)):
+ *        I[t,s] = sum_{j<64} w[t,j] * ReLU(q[t,j] . k[s]),
+ *      64 heads of dim 128, one key per cached token shared by all heads,
+ *      fp8-e4m3fn keys with one fp32 scale per 128-element block (= per
+ *      token); causal: only s <= pos(t) is scored.
+ *   2. Per-query top-k over the valid positions ("详解DSA", Indexer code
+ *      block: topk(min(index_topk, end_pos))), ties toward the lower index.
+ *   3. Sparse MQA-mode MLA ("详解DSA" Eq.(2); MQA mode per the charlestar
+ *      page "DSA 怎样嵌入 MLA" and the luowle page section 3.1): every query
+ *      head attends to the same selected 576-wide latent entries (512 latent
+ *      + 64 rope); the value is the first 512 dims; the softmax runs over the
+ *      selected entries only.
+ *
+ * Geometry and positions.  B sequences, q_len new queries per sequence,
+ * T = B*q_len query rows, row t = b*q_len + i.  seq_lens[b] is the number of
+ * cached tokens of sequence b including its new ones (the end_pos of the
+ * Indexer code block), so query i of sequence b sits at
+ *     pos = seq_lens[b] - q_len + i
+ * and sees the keys s <= pos (inclusive causal mask).  Kernels clamp
+ * seq_lens[b] into [0, S_max]; a row whose pos is negative sees no key.
+ *
+ * Memory.  Every tensor pointer is DEVICE memory allocated and owned by the
+ * caller; all tensors are dense row-major in the shapes given.  The library
+ * never allocates or frees memory and keeps no pointer after the enqueued
+ * work finishes; scratch memory comes in through (ws, ws_bytes), sized by
+ * the matching *_workspace_size query.  Workspace pointers must be 256-byte
+ * aligned, tensor pointers 16-byte aligned.
+ *
+ * Streams and errors.  Every call validates its arguments on the host before
+ * enqueuing anything and returns DSA_ERR_INVALID_ARG (bad pointer, shape,
+ * alignment or size), DSA_ERR_UNSUPPORTED (a dtype combination or size the
+ * kernels do not implement) or DSA_ERR_WORKSPACE (ws too small) without
+ * touching the device.  Otherwise the work is enqueued asynchronously on
+ * `stream` (0 = the null stream) and the call returns DSA_OK, or DSA_ERR_HIP
+ * if a launch failed.  No call synchronises, aborts or throws.  Calls share
+ * no mutable library state; concurrent calls must use distinct workspaces.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DSA_API __attribute__((visibility("default")))
+#else
+#define DSA_API
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1,
+  DSA_ERR_UNSUPPORTED = 2,
+  DSA_ERR_WORKSPACE = 3,
+  DSA_ERR_HIP = 4
+} dsa_status;
+
+typedef enum {
+  DSA_F32 = 0,        /* IEEE binary32 */
+  DSA_BF16 = 1,       /* bfloat16 */
+  DSA_FP8_E4M3FN = 2  /* OCP fp8 e4m3 "fn" (the float8_e4m3fn cache dtype of the Indexer code block) */
+} dsa_dtype;
+
+/* Fixed indexer geometry: the public configuration printed on the luowle
+ * page, section 3.2 (index_n_heads = 64, index_head_dim = 128). */
+#define DSA_INDEX_HEADS 64
+#define DSA_INDEX_DIM 128
+/* Latent entry width and value width of MQA-mode MLA ("详解DSA": 576 = 512
+ * latent + 64 rope; the value is the 512-wide latent). */
+#define DSA_LATENT_DIM 576
+#define DSA_VALUE_DIM 512
+
+typedef struct {
+  int32_t B;                /* sequences, >= 1 */
+  int32_t q_len;            /* new queries per sequence, >= 1 */
+  int32_t S_max;            /* cache capacity per sequence, >= 1 */
+  const int32_t* seq_lens;  /* DEVICE [B]; intended q_len <= seq_lens[b] <= S_max */
+} dsa_geom;
+
+/* Lightning Indexer scores ("详解DSA" Eq.(1), with the fp8 scale handling of
+ * its "DSA计算流" section: the q-scale multiplies each head's ReLU output and
+ * the k-scale multiplies the sum over heads).
+ *
+ *   scores[r, s] = k_scale[b,s] * sum_j w[t,j]*q_scale[t,j]*ReLU(q[t,j,:].k[b,s,:])
+ *                                              for s <= pos(t), s < S_max
+ *   scores[r, s] = -inf                        for pos(t) < s < S_max
+ * with t = row_begin + r, 0 <= r < row_count.  Columns S_max..ld-1 are not
+ * written.
+ *
+ *   q        [T, 64, 128]   FP8_E4M3FN or F32
+ *   q_scale  [T, 64] fp32 or NULL (= 1)
+ *   w        [T, 64]        BF16 or F32, used as given (no extra factors)
+ *   k        [B, S_max, 128] same dtype as q
+ *   k_scale  [B, S_max] fp32 or NULL (= 1)
+ *   scores   [row_count, ld] fp32, ld >= S_max
+ * Supported: (q,k) FP8_E4M3FN with w BF16 or F32; (q,k,w) all F32.
+ * fp8 dot products run on the fp8 matrix cores with fp32 accumulation. */
+DSA_API dsa_status dsa_indexer_scores(const dsa_geom* geom,
+                              const void* q, dsa_dtype q_dtype, const float* q_scale,
+                              const void* w, dsa_dtype w_dtype,
+                              const void* k, dsa_dtype k_dtype, const float* k_scale,
+                              int32_t row_begin, int32_t row_count,
+                              float* scores, int64_t ld, hipStream_t stream);
+
+/* Top-k of precomputed scores ("详解DSA", Indexer code block:
+ * topk(min(index_topk, end_pos)); ties go to the lower position).
+ *
+ * For row r (query t = row_begin + r) the valid set is V = {s : s <= pos(t)}.
+ * If |V| <= k every valid position is selected; otherwise the k positions
+ * that come first in the order (score descending, position ascending).
+ * idx[r, :] holds the selected positions in ASCENDING order followed by -1
+ * padding.  Only columns s <= pos(t) of `scores` are read.  Scores must not
+ * be NaN (NaN rows give an unspecified but in-range selection).
+ *
+ *   scores [row_count, ld] fp32, ld >= S_max;  idx [row_count, k] int32
+ *   1 <= k <= 16384;  ws >= dsa_topk_workspace_size(...) bytes. */
+DSA_API dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld,
+                    int32_t row_begin, int32_t row_count, int32_t k,
+                    int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_topk_workspace_size(int32_t row_count, int32_t S_max, int32_t k);
+
+/* Sparse MQA-mode MLA over selected latent entries ("详解DSA" Eq.(2) and the
+ * masked MLA forward on that page: softmax in fp32 over the selected set).
+ *
+ * For each row t and head h, over M_t = {m : idx[t,m] valid}:
+ *   z_m      = sm_scale * q[t,h,:] . kv[b, idx[t,m], :]          (576 dims)
+ *   out[t,h] = sum_m softmax(z)_m * kv[b, idx[t,m], 0:512]
+ *   lse[t,h] = log sum_m exp(z_m)      (natural log; -inf if M_t is empty)
+ * An index is valid if 0 <= idx <= pos(t); -1 and any other value are skipped
+ * (an empty set gives out = 0).  Duplicated indices count once per copy.
+ *
+ *   q   [T, H, 576]  BF16 or F32     kv [B, S_max, 576] same dtype
+ *   idx [T, k] int32                 out [T, H, 512] same dtype as q
+ *   lse [T, H] fp32 or NULL
+ * H: BF16 needs H % 16 == 0 and H <= 128; F32 needs 1 <= H <= 128.
+ * 1 <= k <= 16384.  ws >= dsa_sparse_mla_workspace_size(...) bytes. */
+DSA_API dsa_status dsa_sparse_mla(const dsa_geom* geom, int32_t H, int32_t k, float sm_scale,
+                          const void* q, dsa_dtype dtype, const void* kv,
+                          const int32_t* idx, void* out, float* lse,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t k,
+                                     dsa_dtype dtype);
+
+/* The whole forward path: indexer -> top-k -> sparse MLA, on one stream.
+ * Arguments as in the three calls above (index_* = the indexer inputs,
+ * mla_* = the attention inputs, both at the same geometry).  idx_out
+ * [T, topk] int32 receives the selection (ascending, -1 padded).
+ *
+ * Long prefills (q_len >= 64 with fp8 inputs) stream the indexer scores
+ * through on-chip memory with a running per-row candidate set, so no T x S
+ * score matrix is ever written; other shapes score into the workspace first.
+ * ws >= dsa_forward_workspace_size(...) bytes. */
+DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale,
+                       const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                       const void* index_w, dsa_dtype index_w_dtype,
+                       const void* index_k, const float* index_k_scale,
+                       const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype,
+                       int32_t* idx_out, void* out, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_forward_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H,
+                                  int32_t topk, dsa_dtype index_dtype, dsa_dtype mla_dtype);
+
+/* Static text for a status code. */
+DSA_API const char* dsa_status_string(dsa_status status);
+
+/* Library version "major.minor.patch". */
+DSA_API const char* dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,241 @@
+"""Python binding of libdsa, the MI355X (gfx950) DSA forward path.
+
+Argument marshalling only: every stage runs in the HIP kernels of libdsa.so
+(built in-tree by ``long_context_lightning_amd.build``).  torch tensors supply
+device memory and the current stream.  Functions mirror the C ABI in
+include/dsa.h and raise ``DsaError`` on any non-OK status.  There is no
+fallback: if the library is missing or fails to load, ``load()`` raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+_STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+           4: "DSA_ERR_HIP"}
+
+_lib = None
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)}")
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("q_len", ctypes.c_int32), ("S_max", ctypes.c_int32),
+                ("seq_lens", ctypes.c_void_p)]
+
+
+def load(path=None):
+    """Load libdsa.so (once).  Raises if it is missing or incomplete."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m long_context_lightning_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    gp = ctypes.POINTER(Geom)
+    sig = {
+        "dsa_indexer_scores": (i32, [gp, vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, vp, i64, vp]),
+        "dsa_topk": (i32, [gp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
+        "dsa_topk_workspace_size": (sz, [i32, i32, i32]),
+        "dsa_sparse_mla": (i32, [gp, i32, i32, f32, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "dsa_sparse_mla_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "dsa_forward": (i32, [gp, i32, i32, f32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz,
+                              vp]),
+        "dsa_forward_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "dsa_status_string": (ctypes.c_char_p, [i32]),
+        "dsa_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)  # AttributeError if the symbol is not exported
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla",
+                 "dsa_sparse_mla_workspace_size", "dsa_forward", "dsa_forward_workspace_size",
+                 "dsa_status_string", "dsa_version")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, where):
+    if status != 0:
+        raise DsaError(status, where)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(t, name, dtypes):
+    _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(t.dtype in dtypes, f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+_FP8 = torch.float8_e4m3fn
+
+
+def _index_dtype(t):
+    # fp8 tensors may come as float8_e4m3fn or as their uint8 codes
+    if t.dtype in (_FP8, torch.uint8):
+        return FP8_E4M3FN
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"indexer tensor dtype {t.dtype} unsupported")
+
+
+def _w_dtype(t):
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"weight dtype {t.dtype} unsupported")
+
+
+def _mla_dtype(t):
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"MLA tensor dtype {t.dtype} unsupported")
+
+
+def make_geom(B, q_len, S_max, seq_lens):
+    """Geometry struct; ``seq_lens`` is an int32 device tensor of length B (kept alive by the caller)."""
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    _need(seq_lens.numel() == B, "seq_lens must have B entries")
+    return Geom(B, q_len, S_max, seq_lens.data_ptr())
+
+
+def indexer_scores(geom, q, w, k, k_scale=None, q_scale=None, row_begin=0, row_count=None, scores=None,
+                   stream=None):
+    """dsa_indexer_scores: returns fp32 scores [row_count, S_max]."""
+    lib = load()
+    T = geom.B * geom.q_len
+    row_count = T - row_begin if row_count is None else row_count
+    _dev(q, "q", (_FP8, torch.uint8, torch.float32))
+    _dev(k, "k", (_FP8, torch.uint8, torch.float32))
+    _dev(w, "w", (torch.bfloat16, torch.int16, torch.uint16, torch.float32))
+    _need(tuple(q.shape) == (T, 64, 128), f"q shape {tuple(q.shape)} != {(T, 64, 128)}")
+    _need(tuple(k.shape) == (geom.B, geom.S_max, 128), "k shape mismatch")
+    _need(tuple(w.shape) == (T, 64), "w shape mismatch")
+    for name, s, shape in (("k_scale", k_scale, (geom.B, geom.S_max)), ("q_scale", q_scale, (T, 64))):
+        if s is not None:
+            _dev(s, name, (torch.float32,))
+            _need(tuple(s.shape) == shape, f"{name} shape mismatch")
+    if scores is None:
+        scores = torch.empty((row_count, geom.S_max), dtype=torch.float32, device=q.device)
+    _dev(scores, "scores", (torch.float32,))
+    _need(scores.dim() == 2 and scores.shape[0] >= row_count, "scores too small")
+    st = lib.dsa_indexer_scores(ctypes.byref(geom), _ptr(q), _index_dtype(q), _ptr(q_scale), _ptr(w), _w_dtype(w),
+                                _ptr(k), _index_dtype(k), _ptr(k_scale), row_begin, row_count, _ptr(scores),
+                                scores.stride(0), _stream(stream))
+    _check(st, "dsa_indexer_scores")
+    return scores
+
+
+def topk_workspace_size(row_count, S_max, k):
+    return int(load().dsa_topk_workspace_size(row_count, S_max, k))
+
+
+def topk(geom, scores, k, row_begin=0, row_count=None, idx=None, ws=None, stream=None):
+    """dsa_topk: returns int32 indices [row_count, k] (ascending, -1 padded)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    row_count = T - row_begin if row_count is None else row_count
+    _dev(scores, "scores", (torch.float32,))
+    if idx is None:
+        idx = torch.empty((row_count, k), dtype=torch.int32, device=scores.device)
+    _dev(idx, "idx", (torch.int32,))
+    need = topk_workspace_size(row_count, geom.S_max, k)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=scores.device)
+    st = lib.dsa_topk(ctypes.byref(geom), _ptr(scores), scores.stride(0), row_begin, row_count, k, _ptr(idx),
+                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_topk")
+    return idx
+
+
+def sparse_mla_workspace_size(B, q_len, H, k, dtype):
+    return int(load().dsa_sparse_mla_workspace_size(B, q_len, H, k, dtype))
+
+
+def sparse_mla(geom, q, kv, idx, sm_scale, out=None, lse=None, ws=None, want_lse=True, stream=None):
+    """dsa_sparse_mla: returns (out [T, H, 512], lse [T, H] or None)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    _dev(q, "q", (torch.bfloat16, torch.float32, torch.int16, torch.uint16))
+    _dev(kv, "kv", (q.dtype,))
+    _dev(idx, "idx", (torch.int32,))
+    _need(q.dim() == 3 and q.shape[0] == T and q.shape[2] == 576, "q must be [T, H, 576]")
+    _need(tuple(kv.shape) == (geom.B, geom.S_max, 576), "kv must be [B, S_max, 576]")
+    _need(idx.dim() == 2 and idx.shape[0] == T, "idx must be [T, k]")
+    H, k = q.shape[1], idx.shape[1]
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    dt = _mla_dtype(q)
+    need = sparse_mla_workspace_size(geom.B, geom.q_len, H, k, dt)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.dsa_sparse_mla(ctypes.byref(geom), H, k, float(sm_scale), _ptr(q), dt, _ptr(kv), _ptr(idx), _ptr(out),
+                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_sparse_mla")
+    return out, lse
+
+
+def forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype):
+    return int(load().dsa_forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype))
+
+
+def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, index_k_scale=None,
+            index_q_scale=None, idx=None, out=None, lse=None, ws=None, want_lse=True, stream=None):
+    """dsa_forward: indexer -> top-k -> sparse MLA.  Returns (idx, out, lse)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    H = mla_q.shape[1]
+    dev = mla_q.device
+    if idx is None:
+        idx = torch.empty((T, topk_k), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=mla_q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    idt, mdt = _index_dtype(index_q), _mla_dtype(mla_q)
+    need = forward_workspace_size(geom.B, geom.q_len, geom.S_max, H, topk_k, idt, mdt)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    for name, t in (("index_q", index_q), ("index_w", index_w), ("index_k", index_k), ("mla_q", mla_q),
+                    ("mla_kv", mla_kv), ("idx", idx), ("out", out)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == (geom.B, geom.S_max, 128),
+          "indexer shapes mismatch")
+    _need(tuple(mla_kv.shape) == (geom.B, geom.S_max, 576) and mla_q.shape[0] == T, "MLA shapes mismatch")
+    st = lib.dsa_forward(ctypes.byref(geom), topk_k, H, float(sm_scale), _ptr(index_q), idt, _ptr(index_q_scale),
+                         _ptr(index_w), _w_dtype(index_w), _ptr(index_k), _ptr(index_k_scale), _ptr(mla_q),
+                         _ptr(mla_kv), mdt, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_forward")
+    return idx, out, lse

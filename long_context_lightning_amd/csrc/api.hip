@@ -1,0 +1,316 @@
+// Host side of the C ABI declared in include/dsa.h: argument validation,
+// workspace carving and the order of launches.  No allocation, no
+// synchronisation, no exceptions across the boundary.
+#include "dsa_internal.h"
+
+namespace dsa {
+bool topk_supported(int S_max, int k);
+bool mla_f32_supported(int k);
+bool prefill_supported(int q_len, int S_max, int k);
+size_t prefill_workspace_bytes(int B, int q_len, int S_max, int k);
+hipError_t launch_indexer_topk_prefill(const IndexerArgs& ia, int k, int32_t* idx, void* ws, hipStream_t s);
+}  // namespace dsa
+
+using namespace dsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRowsPerLaunch = 32768;
+constexpr size_t kScoreChunkBytes = (size_t)256 << 20;
+constexpr int kMaxMlaK = 16384;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline dsa_status hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+bool geom_ok(const dsa_geom* g) {
+  if (!g || g->B < 1 || g->q_len < 1 || g->S_max < 1 || !g->seq_lens) return false;
+  if ((long long)g->B * g->q_len > 0x7FFFFFFFLL) return false;
+  return g->q_len <= g->S_max;
+}
+
+long long rows_of(const dsa_geom* g) { return (long long)g->B * g->q_len; }
+
+bool rows_ok(const dsa_geom* g, int32_t row_begin, int32_t row_count) {
+  return row_begin >= 0 && row_count >= 0 && (long long)row_begin + row_count <= rows_of(g);
+}
+
+dsa_status check_indexer_inputs(const dsa_geom* g, const void* q, dsa_dtype q_dt, const float* q_scale,
+                                const void* w, dsa_dtype w_dt, const void* k, dsa_dtype k_dt,
+                                const float* k_scale) {
+  if (!geom_ok(g) || !q || !w || !k) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(w, 4)) return DSA_ERR_INVALID_ARG;
+  if ((q_scale && !aligned(q_scale, 4)) || (k_scale && !aligned(k_scale, 4))) return DSA_ERR_INVALID_ARG;
+  if (q_dt != k_dt) return DSA_ERR_UNSUPPORTED;
+  if (q_dt == DSA_FP8_E4M3FN) return (w_dt == DSA_BF16 || w_dt == DSA_F32) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+  if (q_dt == DSA_F32) return w_dt == DSA_F32 ? DSA_OK : DSA_ERR_UNSUPPORTED;
+  return DSA_ERR_UNSUPPORTED;
+}
+
+IndexerArgs make_indexer_args(const dsa_geom* g, const void* q, const float* q_scale, const void* w,
+                              dsa_dtype w_dt, const void* k, const float* k_scale) {
+  IndexerArgs a;
+  a.B = g->B;
+  a.q_len = g->q_len;
+  a.S_max = g->S_max;
+  a.seq_lens = g->seq_lens;
+  a.q = q;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.w_is_bf16 = (w_dt == DSA_BF16);
+  a.k = k;
+  a.k_scale = k_scale;
+  a.row_begin = 0;
+  a.row_count = 0;
+  a.scores = nullptr;
+  a.ld = 0;
+  return a;
+}
+
+// The score kernels launch at most kMaxRowsPerLaunch rows at a time.
+hipError_t run_indexer(const IndexerArgs& a, bool fp8, hipStream_t stream) {
+  const int end = a.row_begin + a.row_count;
+  for (int r0 = a.row_begin; r0 < end; r0 += kMaxRowsPerLaunch) {
+    IndexerArgs c = a;
+    c.row_begin = r0;
+    c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
+    c.scores = a.scores + (long long)(r0 - a.row_begin) * a.ld;
+    const hipError_t e = fp8 ? launch_indexer_fp8(c, stream) : launch_indexer_f32(c, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Top-k over kMaxRowsPerLaunch-row chunks; each chunk reuses the same workspace.
+hipError_t run_topk(const TopkArgs& a, hipStream_t stream) {
+  const int end = a.row_begin + a.row_count;
+  for (int r0 = a.row_begin; r0 < end; r0 += kMaxRowsPerLaunch) {
+    TopkArgs c = a;
+    c.row_begin = r0;
+    c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
+    c.scores = a.scores + (long long)(r0 - a.row_begin) * a.ld;
+    c.idx = a.idx + (long long)(r0 - a.row_begin) * a.k;
+    const hipError_t e = launch_topk(c, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t run_mla(const MlaArgs& a, bool bf16, hipStream_t stream) {
+  if (bf16) return launch_mla_bf16(a, stream);
+  const int end = a.row_begin + a.row_count;
+  for (int r0 = a.row_begin; r0 < end; r0 += kMaxRowsPerLaunch) {
+    MlaArgs c = a;
+    c.row_begin = r0;
+    c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
+    const hipError_t e = launch_mla_f32(c, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+dsa_status check_mla(const dsa_geom* g, int32_t H, int32_t k, const void* q, dsa_dtype dt, const void* kv,
+                     const int32_t* idx, const void* out, const float* lse) {
+  if (!geom_ok(g) || !q || !kv || !idx || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(idx, 4)) return DSA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return DSA_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxMlaK || H < 1 || H > 128) return DSA_ERR_INVALID_ARG;
+  if (dt == DSA_BF16) return (H % 16 == 0) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+  if (dt == DSA_F32) return mla_f32_supported(k) ? DSA_OK : DSA_ERR_UNSUPPORTED;
+  return DSA_ERR_UNSUPPORTED;
+}
+
+MlaArgs make_mla_args(const dsa_geom* g, int32_t H, int32_t k, float sm_scale, const void* q, const void* kv,
+                      const int32_t* idx, void* out, float* lse, void* ws) {
+  MlaArgs a;
+  a.B = g->B;
+  a.q_len = g->q_len;
+  a.S_max = g->S_max;
+  a.H = H;
+  a.k = k;
+  a.seq_lens = g->seq_lens;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.kv = kv;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.ws = ws;
+  a.row_begin = 0;
+  a.row_count = (int)rows_of(g);
+  return a;
+}
+
+// Workspace plan of dsa_forward.
+struct ForwardPlan {
+  bool streaming;
+  int chunk_rows;
+  size_t scores_off, topk_off, mla_off, total;
+};
+
+ForwardPlan plan_forward(int B, int q_len, int S_max, int H, int topk, dsa_dtype index_dt, dsa_dtype mla_dt) {
+  ForwardPlan p{};
+  const long long T = (long long)B * q_len;
+  p.streaming = index_dt == DSA_FP8_E4M3FN && q_len >= 64 && prefill_supported(q_len, S_max, topk);
+  size_t off = 0;
+  if (p.streaming) {
+    p.chunk_rows = 0;
+    p.scores_off = p.topk_off = 0;
+    off = align_up(prefill_workspace_bytes(B, q_len, S_max, topk));
+  } else {
+    long long rows = (long long)(kScoreChunkBytes / ((size_t)S_max * 4));
+    if (rows < 1) rows = 1;
+    if (rows > T) rows = T;
+    if (rows > kMaxRowsPerLaunch) rows = kMaxRowsPerLaunch;
+    p.chunk_rows = (int)rows;
+    p.scores_off = 0;
+    off = align_up((size_t)rows * S_max * 4);
+    p.topk_off = off;
+    off += align_up(topk_workspace_bytes((int)rows, S_max, topk));
+  }
+  p.mla_off = off;
+  off += align_up(mla_workspace_bytes((int)T, H, topk, mla_dt == DSA_BF16));
+  p.total = off;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_scores(const dsa_geom* geom, const void* q, dsa_dtype q_dtype, const float* q_scale,
+                              const void* w, dsa_dtype w_dtype, const void* k, dsa_dtype k_dtype,
+                              const float* k_scale, int32_t row_begin, int32_t row_count, float* scores,
+                              int64_t ld, hipStream_t stream) {
+  const dsa_status st = check_indexer_inputs(geom, q, q_dtype, q_scale, w, w_dtype, k, k_dtype, k_scale);
+  if (st != DSA_OK) return st;
+  if (!rows_ok(geom, row_begin, row_count) || ld < geom->S_max) return DSA_ERR_INVALID_ARG;
+  if (row_count == 0) return DSA_OK;
+  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
+  IndexerArgs a = make_indexer_args(geom, q, q_scale, w, w_dtype, k, k_scale);
+  a.row_begin = row_begin;
+  a.row_count = row_count;
+  a.scores = scores;
+  a.ld = ld;
+  return hip_status(run_indexer(a, q_dtype == DSA_FP8_E4M3FN, stream));
+}
+
+size_t dsa_topk_workspace_size(int32_t row_count, int32_t S_max, int32_t k) {
+  if (row_count <= 0 || S_max <= 0 || k <= 0) return 0;
+  const int rows = row_count < kMaxRowsPerLaunch ? row_count : kMaxRowsPerLaunch;
+  return topk_workspace_bytes(rows, S_max, k);
+}
+
+dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld, int32_t row_begin, int32_t row_count,
+                    int32_t k, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!geom_ok(geom) || !rows_ok(geom, row_begin, row_count) || ld < geom->S_max || k < 1)
+    return DSA_ERR_INVALID_ARG;
+  if (row_count == 0) return DSA_OK;
+  if (!scores || !idx || !aligned(scores, 4) || !aligned(idx, 4)) return DSA_ERR_INVALID_ARG;
+  if (!topk_supported(geom->S_max, k)) return DSA_ERR_UNSUPPORTED;
+  const size_t need = dsa_topk_workspace_size(row_count, geom->S_max, k);
+  if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
+  TopkArgs a;
+  a.B = geom->B;
+  a.q_len = geom->q_len;
+  a.S_max = geom->S_max;
+  a.seq_lens = geom->seq_lens;
+  a.scores = scores;
+  a.ld = ld;
+  a.row_begin = row_begin;
+  a.row_count = row_count;
+  a.k = k;
+  a.idx = idx;
+  a.ws = ws;
+  return hip_status(run_topk(a, stream));
+}
+
+size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t k, dsa_dtype dtype) {
+  if (B < 1 || q_len < 1 || H < 1 || k < 1) return 0;
+  return mla_workspace_bytes(B * q_len, H, k, dtype == DSA_BF16);
+}
+
+dsa_status dsa_sparse_mla(const dsa_geom* geom, int32_t H, int32_t k, float sm_scale, const void* q,
+                          dsa_dtype dtype, const void* kv, const int32_t* idx, void* out, float* lse, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  const dsa_status st = check_mla(geom, H, k, q, dtype, kv, idx, out, lse);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa_sparse_mla_workspace_size(geom->B, geom->q_len, H, k, dtype);
+  if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
+  const MlaArgs a = make_mla_args(geom, H, k, sm_scale, q, kv, idx, out, lse, ws);
+  return hip_status(run_mla(a, dtype == DSA_BF16, stream));
+}
+
+size_t dsa_forward_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t topk,
+                                  dsa_dtype index_dtype, dsa_dtype mla_dtype) {
+  if (B < 1 || q_len < 1 || S_max < 1 || H < 1 || topk < 1) return 0;
+  return plan_forward(B, q_len, S_max, H, topk, index_dtype, mla_dtype).total;
+}
+
+dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale, const void* index_q,
+                       dsa_dtype index_dtype, const float* index_q_scale, const void* index_w,
+                       dsa_dtype index_w_dtype, const void* index_k, const float* index_k_scale,
+                       const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype, int32_t* idx_out, void* out,
+                       float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  dsa_status st = check_indexer_inputs(geom, index_q, index_dtype, index_q_scale, index_w, index_w_dtype, index_k,
+                                       index_dtype, index_k_scale);
+  if (st != DSA_OK) return st;
+  if (!idx_out || !aligned(idx_out, 4) || topk < 1) return DSA_ERR_INVALID_ARG;
+  st = check_mla(geom, H, topk, mla_q, mla_dtype, mla_kv, idx_out, out, lse);
+  if (st != DSA_OK) return st;
+  const ForwardPlan p = plan_forward(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype);
+  if (!p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+  const int T = (int)rows_of(geom);
+  IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
+  hipError_t e = hipSuccess;
+  if (p.streaming) {
+    ia.row_begin = 0;
+    ia.row_count = T;
+    e = launch_indexer_topk_prefill(ia, topk, idx_out, wsb, stream);
+  } else {
+    float* scores = reinterpret_cast<float*>(wsb + p.scores_off);
+    for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
+      const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
+      ia.row_begin = r0;
+      ia.row_count = rc;
+      ia.scores = scores;
+      ia.ld = geom->S_max;
+      e = run_indexer(ia, index_dtype == DSA_FP8_E4M3FN, stream);
+      if (e != hipSuccess) break;
+      TopkArgs ta;
+      ta.B = geom->B;
+      ta.q_len = geom->q_len;
+      ta.S_max = geom->S_max;
+      ta.seq_lens = geom->seq_lens;
+      ta.scores = scores;
+      ta.ld = geom->S_max;
+      ta.row_begin = r0;
+      ta.row_count = rc;
+      ta.k = topk;
+      ta.idx = idx_out + (long long)r0 * topk;
+      ta.ws = wsb + p.topk_off;
+      e = run_topk(ta, stream);
+    }
+  }
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  const MlaArgs ma = make_mla_args(geom, H, topk, sm_scale, mla_q, mla_kv, idx_out, out, lse, wsb + p.mla_off);
+  return hip_status(run_mla(ma, mla_dtype == DSA_BF16, stream));
+}
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG: bad pointer, shape, alignment or size";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED: dtype combination or size not implemented";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown dsa_status";
+}
+
+const char* dsa_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Internal declarations shared by the HIP translation units of libdsa.
+// Not part of the public ABI (include/dsa.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int kHI = DSA_INDEX_HEADS;   // indexer heads
+constexpr int kDI = DSA_INDEX_DIM;     // indexer head dim
+constexpr int kDQK = DSA_LATENT_DIM;   // latent entry width
+constexpr int kDV = DSA_VALUE_DIM;     // value width
+
+// ---------------------------------------------------------------- helpers
+
+// Monotone map fp32 -> uint32: a < b (as floats, no NaN) <=> key(a) < key(b).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Length of sequence b clamped into [0, S_max].
+__device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int S_max) {
+  int L = seq_lens[b];
+  return L < 0 ? 0 : (L > S_max ? S_max : L);
+}
+
+// Position of query row t (may be negative: the row then sees no key).
+__device__ __forceinline__ int row_pos(const int32_t* seq_lens, int t, int q_len, int S_max) {
+  int b = t / q_len;
+  return clamped_len(seq_lens, b, S_max) - q_len + (t - b * q_len);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Sum of v over the lanes l and l^16 / l^32 using the gfx950 row-swap ops.
+__device__ __forceinline__ float sum_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// ------------------------------------------------------------ launch args
+
+struct IndexerArgs {
+  int B, q_len, S_max;
+  const int32_t* seq_lens;
+  const void* q;          // [T,64,128] fp8 codes or f32
+  const float* q_scale;   // [T,64] or null
+  const void* w;          // [T,64] bf16 or f32
+  int w_is_bf16;
+  const void* k;          // [B,S_max,128] fp8 codes or f32
+  const float* k_scale;   // [B,S_max] or null
+  int row_begin, row_count;
+  float* scores;          // [row_count, ld]
+  long long ld;
+};
+
+hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t s);
+hipError_t launch_indexer_f32(const IndexerArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  int B, q_len, S_max;
+  const int32_t* seq_lens;
+  const float* scores;    // [row_count, ld]
+  long long ld;
+  int row_begin, row_count, k;
+  int32_t* idx;           // [row_count, k]
+  void* ws;
+};
+
+size_t topk_workspace_bytes(int row_count, int S_max, int k);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+
+struct MlaArgs {
+  int B, q_len, S_max, H, k;
+  const int32_t* seq_lens;
+  float sm_scale;
+  const void* q;          // [T,H,576]
+  const void* kv;         // [B,S_max,576]
+  const int32_t* idx;     // [T,k]
+  void* out;              // [T,H,512]
+  float* lse;             // [T,H] or null
+  void* ws;
+  int row_begin, row_count;  // rows handled by this launch
+};
+
+size_t mla_workspace_bytes(int T, int H, int k, int is_bf16);
+hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t s);
+hipError_t launch_mla_f32(const MlaArgs& a, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,227 @@
+// Lightning Indexer scores into a row-major score buffer ("详解DSA" Eq.(1)).
+//
+//   I[t,s] = k_scale[s] * sum_j w[t,j]*q_scale[t,j] * ReLU(q[t,j,:] . k[s,:])
+//
+// fp8 path: one wave owns 64 consecutive keys of one sequence and up to NQ
+// query rows of that sequence.  The 64x128 query tile of a row stays in
+// registers as four A fragments of v_mfma_f32_16x16x128_f8f6f4 (16 heads x
+// the full 128-deep dot each), each 16-key block of the fp8 key cache is
+// loaded straight from HBM into a B fragment (four lanes per 128-byte key
+// row, fully coalesced), and four MFMAs give D[64 heads, 16 keys].  The
+// epilogue applies ReLU and the per-head weight in fp32 on the MFMA result
+// registers, then reduces the 64 heads across the four 16-lane rows with the
+// gfx950 row-swap permutes, arranged so that after four key blocks lane l
+// holds the finished score of key (wave_base + l): the k-scale multiply, the
+// causal mask and the store are one coalesced 256-byte row write.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kKeysPerWave = 64;
+constexpr int kKeysPerBlock = kWavesPerBlock * kKeysPerWave;
+
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  v4i lo = *reinterpret_cast<const v4i*>(p);
+  v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// D[16 heads, 16 keys] = A (heads x 128 fp8) * B (128 fp8 x keys); fp32 accumulate.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+// Row group handled by this block: up to NQ consecutive rows of one sequence.
+struct RowGroup {
+  int b, t0, nr;
+};
+
+template <int NQ>
+__device__ __forceinline__ RowGroup row_group(const IndexerArgs& a) {
+  const int row_end = a.row_begin + a.row_count;
+  const int gps = (a.q_len + NQ - 1) / NQ;
+  const int b = a.row_begin / a.q_len + (int)blockIdx.y / gps;
+  const int j = (int)blockIdx.y % gps;
+  int t0 = b * a.q_len + j * NQ;
+  int t1 = min(t0 + NQ, (b + 1) * a.q_len);
+  t0 = max(t0, a.row_begin);
+  t1 = min(t1, row_end);
+  return RowGroup{b, t0, t1 - t0};
+}
+
+template <int NQ, bool WBF16>
+__global__ __launch_bounds__(256) void k_indexer_fp8(IndexerArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const RowGroup rg = row_group<NQ>(a);
+  if (rg.nr <= 0 || rg.b >= a.B) return;
+  const int L = clamped_len(a.seq_lens, rg.b, a.S_max);
+  const int qi0 = rg.t0 - rg.b * a.q_len;
+  int pos[NQ];
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) pos[r] = (r < rg.nr) ? L - a.q_len + qi0 + r : -1;
+  const int maxpos = L - a.q_len + qi0 + rg.nr - 1;
+
+  const int kw = (int)blockIdx.x * kKeysPerBlock + wave * kKeysPerWave;
+  if (kw >= a.S_max) return;
+  const int s_l = kw + lane;  // key whose finished score this lane stores
+  float* out = a.scores + (long long)(rg.t0 - a.row_begin) * a.ld;
+  if (kw > maxpos) {  // the whole wave is beyond every row's position
+    if (s_l < a.S_max)
+      for (int r = 0; r < rg.nr; ++r) out[(long long)r * a.ld + s_l] = -INFINITY;
+    return;
+  }
+
+  // Key fragments first so the HBM stream starts as early as possible.
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
+  v8i kf[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int s = kw + 16 * blk + c;
+    kf[blk] = (s < a.S_max) ? load32(kb + (size_t)s * kDI + 32 * g) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const float ks = (a.k_scale && s_l < a.S_max) ? a.k_scale[(size_t)rg.b * a.S_max + s_l] : 1.0f;
+
+  // Query fragments (row = head 16m+c, bytes 32g..32g+31) and head weights of
+  // the output rows this lane holds (heads 16m + 4g + i).
+  const uint8_t* qb = static_cast<const uint8_t*>(a.q);
+  v8i qf[NQ][4];
+  float wv[NQ][4][4];
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) {
+    const int t = rg.t0 + r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (r < rg.nr) {
+        qf[r][m] = load32(qb + ((size_t)t * kHI + 16 * m + c) * kDI + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 16 * m + 4 * g + i;
+          float wt;
+          if (WBF16)
+            wt = bf16_to_f32(static_cast<const uint16_t*>(a.w)[(size_t)t * kHI + h]);
+          else
+            wt = static_cast<const float*>(a.w)[(size_t)t * kHI + h];
+          if (a.q_scale) wt *= a.q_scale[(size_t)t * kHI + h];
+          wv[r][m][i] = wt;
+        }
+      } else {
+        qf[r][m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[r][m][i] = 0.f;
+      }
+    }
+  }
+
+  float x[NQ][4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v4f d = mfma_fp8_16x16x128(qf[r][m], kf[blk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], fmaxf(d[i], 0.f), acc);
+      }
+      x[r][blk] = acc;
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < NQ; ++r) {
+    // Transpose-reduce over the four 16-lane rows: afterwards lane (g, c)
+    // holds the head sum of block g, key column c, i.e. key kw + lane.
+    auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][0]), __float_as_uint(x[r][1]), false, false);
+    auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][2]), __float_as_uint(x[r][3]), false, false);
+    const float a01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+    const float a23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+    auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+    const float tot = __uint_as_float(pf[0]) + __uint_as_float(pf[1]);
+    if (r < rg.nr && s_l < a.S_max)
+      out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? tot * ks : -INFINITY;
+  }
+}
+
+// fp32 path (tiny configuration): one block per (row, 256-key tile), the query
+// row staged in LDS, one thread per key.
+__global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
+  __shared__ float qs[kHI * kDI];
+  __shared__ float wsh[kHI];
+  const int t = a.row_begin + (int)blockIdx.y;
+  const int b = t / a.q_len;
+  const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);
+  const int tile0 = (int)blockIdx.x * 256;
+  const int s = tile0 + (int)threadIdx.x;
+  float* out = a.scores + (long long)(t - a.row_begin) * a.ld;
+  if (tile0 > pos) {
+    if (s < a.S_max) out[s] = -INFINITY;
+    return;
+  }
+  const float* qrow = static_cast<const float*>(a.q) + (size_t)t * kHI * kDI;
+  for (int e = threadIdx.x; e < kHI * kDI; e += 256) qs[e] = qrow[e];
+  if (threadIdx.x < kHI) {
+    float wt = a.w_is_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.w)[(size_t)t * kHI + threadIdx.x])
+                           : static_cast<const float*>(a.w)[(size_t)t * kHI + threadIdx.x];
+    if (a.q_scale) wt *= a.q_scale[(size_t)t * kHI + threadIdx.x];
+    wsh[threadIdx.x] = wt;
+  }
+  __syncthreads();
+  if (s >= a.S_max) return;
+  if (s > pos) {
+    out[s] = -INFINITY;
+    return;
+  }
+  const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + ((size_t)b * a.S_max + s) * kDI);
+  float kreg[kDI];
+#pragma unroll
+  for (int d = 0; d < kDI / 4; ++d) {
+    const float4 v = kr[d];
+    kreg[4 * d] = v.x; kreg[4 * d + 1] = v.y; kreg[4 * d + 2] = v.z; kreg[4 * d + 3] = v.w;
+  }
+  float score = 0.f;
+  for (int j = 0; j < kHI; ++j) {
+    float dot = 0.f;
+#pragma unroll
+    for (int d = 0; d < kDI; ++d) dot = fmaf(qs[j * kDI + d], kreg[d], dot);
+    score = fmaf(wsh[j], fmaxf(dot, 0.f), score);
+  }
+  const float ksc = a.k_scale ? a.k_scale[(size_t)b * a.S_max + s] : 1.0f;
+  out[s] = score * ksc;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t stream) {
+  if (a.row_count <= 0) return hipSuccess;
+  const int b0 = a.row_begin / a.q_len;
+  const int b1 = (a.row_begin + a.row_count - 1) / a.q_len;
+  const dim3 block(256);
+  const unsigned gx = (unsigned)((a.S_max + kKeysPerBlock - 1) / kKeysPerBlock);
+  if (a.q_len == 1) {
+    const dim3 grid(gx, (unsigned)(b1 - b0 + 1));
+    if (a.w_is_bf16) hipLaunchKernelGGL((k_indexer_fp8<1, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_indexer_fp8<1, false>), grid, block, 0, stream, a);
+  } else {
+    const int gps = (a.q_len + 1) / 2;
+    const dim3 grid(gx, (unsigned)((b1 - b0 + 1) * gps));
+    if (a.w_is_bf16) hipLaunchKernelGGL((k_indexer_fp8<2, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((k_indexer_fp8<2, false>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_f32(const IndexerArgs& a, hipStream_t stream) {
+  if (a.row_count <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((a.S_max + 255) / 256), (unsigned)a.row_count);
+  hipLaunchKernelGGL(k_indexer_f32, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,380 @@
+// Fused long-prefill indexer + streaming top-k.
+//
+// The charlestar page ("Prefill 与 decode 中发生了什么", Prefill) asks for
+// tile-wise index scores with local candidates kept on chip, hierarchical
+// merging into the final top-k, and no full L x L score matrix written to
+// HBM.  This kernel does exactly that on gfx950:
+//
+//  * A block owns 16 consecutive query rows of one sequence (two per wave)
+//    and walks the causal key range [0, max_pos] in 64-key tiles staged
+//    through LDS (double buffered; 144-byte padded rows so the MFMA B-operand
+//    reads of 16 different keys hit distinct banks).
+//  * Scores: v_mfma_f32_16x16x128_f8f6f4 with the query rows' 64x128 fp8
+//    tiles held in registers; ReLU, per-head weight and the reduction over
+//    the 64 heads are fused on the MFMA result registers; the k-scale and
+//    the causal mask are applied to the finished 64 scores (one per lane).
+//  * Selection: each row keeps a running threshold theta (an order-preserving
+//    uint32 image of an fp32 score) and a candidate list in the workspace.
+//    A score is appended (in position order) only if it beats theta.  When
+//    lists fill up, the owning waves compact them: an exact radix select
+//    finds the k-th largest key tau of the list, the list keeps the entries
+//    above tau plus the lowest-position copies of tau, and theta := tau.
+//    Later scores equal to tau can never win (their positions are larger),
+//    so the rule "score desc, position asc" is preserved exactly.  At the end
+//    a last exact compaction leaves the top-k in ascending position order.
+//  * Rows with pos + 1 <= k keep every position (no scoring needed); blocks
+//    whose rows are all that short skip the GEMM.
+//
+// Blocks are issued longest-row-first so the causal triangle load-balances.
+#include "block_scan.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kRows = 16;         // query rows per block
+constexpr int kWaves = 8;         // two rows per wave
+constexpr int kThreads = kWaves * 64;
+constexpr int kNK = 64;           // keys per tile
+constexpr int kKRS = 144;         // LDS stride of one 128-byte key row
+constexpr int kMaxK = 4096;
+
+__host__ __device__ inline int cand_cap(int k) {
+  int extra = k / 2 > 1024 ? k / 2 : 1024;
+  return (k + extra + 63) / 64 * 64;
+}
+
+__device__ __forceinline__ v8i lds_load32(const unsigned char* p) {
+  const v4i lo = *reinterpret_cast<const v4i*>(p);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ v8i glb_load32(const uint8_t* p) {
+  const v4i lo = *reinterpret_cast<const v4i*>(p);
+  const v4i hi = *reinterpret_cast<const v4i*>(p + 16);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ v4f mfma_fp8(v8i a, v8i b) {
+  v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, z, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void wave_sync_mem() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// Exact compaction of one row's candidate list by one wave.
+// Keeps the `want` best entries under (key desc, position asc), in the
+// original (position-ascending) order.  Returns tau, the smallest kept key
+// (0 if nothing was dropped).  `hist` is this wave's 256-word LDS area.
+__device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int want, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  if (n <= want) return 0u;
+  wave_sync_mem();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = lane; i < n; i += 64) {
+    const uint32_t u = ekey[i];
+    mn = min(mn, u);
+    mx = max(mx, u);
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  uint32_t tau = mn, rem = (uint32_t)want;
+  if (mn != mx) {
+    const int common = __clz(mn ^ mx);  // leading bits shared by every key
+    int rem_bits = 32 - common;
+    uint32_t prefix = common == 0 ? 0u : (mn & (0xFFFFFFFFu << rem_bits));
+    while (rem_bits > 0) {
+      const int nb = rem_bits < 8 ? rem_bits : 8;
+      const int shift = rem_bits - nb;
+      const uint32_t dmask = (1u << nb) - 1u;
+      for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+      wave_sync_mem();
+      const uint32_t hi = rem_bits >= 32 ? 0u : prefix >> rem_bits;
+      for (int i = lane; i < n; i += 64) {
+        const uint32_t u = ekey[i];
+        if ((rem_bits >= 32 ? 0u : u >> rem_bits) == hi) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+      }
+      wave_sync_mem();
+      const int d0 = 4 * (63 - lane);
+      uint32_t c[4], tot = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[d0 + 3 - j];
+        tot += c[j];
+      }
+      const uint32_t above = wave_inclusive_sum(tot) - tot;
+      uint32_t dsel = 0, asel = 0;
+      const bool mine = above < rem && rem <= above + tot;
+      if (mine) {
+        uint32_t acc = above;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (acc < rem && rem <= acc + c[j]) {
+            dsel = (uint32_t)(d0 + 3 - j);
+            asel = acc;
+          }
+          acc += c[j];
+        }
+      }
+      const unsigned long long who = __ballot(mine);
+      const int src = __ffsll((long long)who) - 1;
+      dsel = (uint32_t)__shfl((int)dsel, src, 64);
+      asel = (uint32_t)__shfl((int)asel, src, 64);
+      prefix |= dsel << shift;
+      rem -= asel;
+      rem_bits = shift;
+      wave_sync_mem();
+    }
+    tau = prefix;
+  }
+  // Stable in-place compaction: keep key > tau and the first `rem` copies of tau.
+  int w = 0;
+  uint32_t eq_seen = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    uint32_t u = 0, p = 0;
+    if (i < n) {
+      u = ekey[i];
+      p = eidx[i];
+    }
+    const bool eq = i < n && u == tau;
+    const unsigned long long eqb = __ballot(eq);
+    const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqb & lt);
+    const bool keep = i < n && (u > tau || (eq && eq_rank < rem));
+    const unsigned long long kb = __ballot(keep);
+    if (keep) {
+      const int slot = w + __popcll(kb & lt);
+      ekey[slot] = u;
+      eidx[slot] = p;
+    }
+    w += __popcll(kb);
+    eq_seen += (uint32_t)__popcll(eqb);
+  }
+  n = w;
+  wave_sync_mem();
+  return tau;
+}
+
+__global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kNK * kKRS];
+  __shared__ float ksc[2][kNK];
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ int need_compact;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
+  // Longest rows first: block j -> query block (nqb-1-j/B) of sequence j%B.
+  const int nqb = (a.q_len + kRows - 1) / kRows;
+  const int b = (int)blockIdx.x % a.B;
+  const int qb = nqb - 1 - (int)blockIdx.x / a.B;
+  const int L = clamped_len(a.seq_lens, b, a.S_max);
+  const int i0 = qb * kRows;                       // first query index in the sequence
+  const int nrows = min(kRows, a.q_len - i0);
+  const int t_base = b * a.q_len + i0;
+  const int maxpos = L - a.q_len + i0 + nrows - 1;  // position of the last row
+
+  // This wave's two rows.
+  int rpos[2];
+  bool rvalid[2];
+  int rt[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const int ri = 2 * wave + rr;
+    rvalid[rr] = ri < nrows;
+    rt[rr] = t_base + ri;
+    rpos[rr] = rvalid[rr] ? L - a.q_len + i0 + ri : -1;
+  }
+
+  if (maxpos + 1 <= k) {  // every row keeps all of its positions
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      if (!rvalid[rr]) continue;
+      int32_t* out = idx_out + (size_t)rt[rr] * k;
+      for (int j = lane; j < k; j += 64) out[j] = (j <= rpos[rr]) ? j : -1;
+    }
+    return;
+  }
+
+  // Candidate lists of this wave's rows.
+  uint32_t* ekey[2];
+  uint32_t* eidx[2];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    uint32_t* base = static_cast<uint32_t*>(ws) + (size_t)(rt[rr] - a.row_begin) * 2 * cap;
+    ekey[rr] = base;
+    eidx[rr] = base + cap;
+  }
+  int n[2] = {0, 0};
+  uint32_t theta[2] = {0u, 0u};  // below every real key: everything valid enters
+
+  // Query fragments and head weights (heads 16m + 4g + i of the MFMA output rows).
+  const uint8_t* qb8 = static_cast<const uint8_t*>(a.q);
+  v8i qf[2][4];
+  float wv[2][4][4];
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      if (rvalid[rr]) {
+        const size_t t = (size_t)rt[rr];
+        qf[rr][m] = glb_load32(qb8 + (t * kHI + 16 * m + c) * kDI + 32 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 16 * m + 4 * g + i;
+          float wt = a.w_is_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.w)[t * kHI + h])
+                                 : static_cast<const float*>(a.w)[t * kHI + h];
+          if (a.q_scale) wt *= a.q_scale[t * kHI + h];
+          wv[rr][m][i] = wt;
+        }
+      } else {
+        qf[rr][m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wv[rr][m][i] = 0.f;
+      }
+    }
+
+  // Key tile staging: thread tid moves 16 bytes (key tid/8, chunk tid%8).
+  const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (size_t)b * a.S_max * kDI;
+  const float* ksb = a.k_scale ? a.k_scale + (size_t)b * a.S_max : nullptr;
+  const int ntiles = (maxpos + kNK) / kNK;
+  const int st_key = tid >> 3, st_chunk = tid & 7;
+  v4i pre;
+  float pre_sc = 1.f;
+  auto fetch = [&](int ti) {
+    const int s = ti * kNK + st_key;
+    pre = (s <= maxpos) ? *reinterpret_cast<const v4i*>(kb8 + (size_t)s * kDI + 16 * st_chunk) : v4i{0, 0, 0, 0};
+    if (tid < kNK) {
+      const int s2 = ti * kNK + tid;
+      pre_sc = (ksb && s2 <= maxpos) ? ksb[s2] : 1.f;
+    }
+  };
+  auto stage = [&](int buf) {
+    *reinterpret_cast<v4i*>(&ktile[buf][st_key * kKRS + 16 * st_chunk]) = pre;
+    if (tid < kNK) ksc[buf][tid] = pre_sc;
+  };
+
+  if (tid == 0) need_compact = 0;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int ti = 0; ti < ntiles; ++ti) {
+    const int buf = ti & 1;
+    const int tile0 = ti * kNK;
+    if (ti + 1 < ntiles) fetch(ti + 1);
+
+    const bool act0 = rpos[0] >= tile0, act1 = rpos[1] >= tile0;
+    if (act0 || act1) {
+      float x[2][4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const v8i kf = lds_load32(&ktile[buf][(16 * blk + c) * kKRS + 32 * g]);
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+          float acc = 0.f;
+          if (rr == 0 ? act0 : act1) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              const v4f d = mfma_fp8(qf[rr][m], kf);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc = fmaf(wv[rr][m][i], fmaxf(d[i], 0.f), acc);
+            }
+          }
+          x[rr][blk] = acc;
+        }
+      }
+      const float ks = ksc[buf][lane];
+      const int s = tile0 + lane;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        if (!(rr == 0 ? act0 : act1)) continue;
+        auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[rr][0]), __float_as_uint(x[rr][1]), false, false);
+        auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[rr][2]), __float_as_uint(x[rr][3]), false, false);
+        const float a01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+        const float a23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+        auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+        const float score = (__uint_as_float(pf[0]) + __uint_as_float(pf[1])) * ks;
+        const uint32_t u = order_key(score);
+        const bool valid = s <= rpos[rr];
+        const bool pred = valid && u > theta[rr];
+        const unsigned long long ball = __ballot(pred);
+        if (ball) {
+          const int slot = n[rr] + __popcll(ball & lt);
+          if (pred) {
+            ekey[rr][slot] = u;
+            eidx[rr][slot] = (uint32_t)s;
+          }
+          n[rr] += __popcll(ball);
+        }
+      }
+      if (lane == 0 && (n[0] > cap - kNK || n[1] > cap - kNK)) atomicOr(&need_compact, 1);
+    }
+
+    if (ti + 1 < ntiles) stage(buf ^ 1);
+    __syncthreads();
+    if (need_compact) {
+      // Batched: every wave trims its fuller lists so compactions overlap.
+      const int trigger = k + (cap - k) / 2;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        if (n[rr] > trigger) {
+          const uint32_t tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+          theta[rr] = tau;
+        }
+      __syncthreads();
+      if (tid == 0) need_compact = 0;
+      __syncthreads();
+    }
+  }
+
+  // Final exact selection and output (ascending positions, -1 padded).
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    if (!rvalid[rr]) continue;
+    int32_t* out = idx_out + (size_t)rt[rr] * k;
+    if (rpos[rr] + 1 <= k) {
+      for (int j = lane; j < k; j += 64) out[j] = (j <= rpos[rr]) ? j : -1;
+      continue;
+    }
+    wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+    for (int j = lane; j < k; j += 64) out[j] = (j < n[rr]) ? (int32_t)eidx[rr][j] : -1;
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(int q_len, int S_max, int k) {
+  (void)q_len;
+  return k >= 1 && k <= kMaxK && S_max >= 1;
+}
+
+size_t prefill_workspace_bytes(int B, int q_len, int S_max, int k) {
+  (void)S_max;
+  return (size_t)B * q_len * 2 * cand_cap(k) * sizeof(uint32_t);
+}
+
+hipError_t launch_indexer_topk_prefill(const IndexerArgs& a, int k, int32_t* idx, void* ws, hipStream_t stream) {
+  const int nqb = (a.q_len + kRows - 1) / kRows;
+  const dim3 grid((unsigned)(nqb * a.B));
+  hipLaunchKernelGGL(k_prefill, grid, dim3(kThreads), 0, stream, a, k, idx, ws, cand_cap(k));
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,295 @@
+// Top-k over materialised score rows (decode / short rows).
+//
+// Rule ("详解DSA", Indexer code block: topk(min(index_topk, end_pos))):
+// V = {s <= pos}; |V| <= k keeps V; otherwise the k positions first in the
+// order (score desc, position asc).  Output: ascending positions, -1 padded.
+//
+// Four launches, all on the caller's stream:
+//  1. zero   -- clear the per-row histograms and counters in the workspace.
+//  2. hist   -- (row, 8192-score segment) blocks: LDS histogram of the top 12
+//               bits of each score's order key, flushed with global atomics.
+//  3. gather -- same blocks: every block finds the threshold bin b* (the bin
+//               holding the k-th largest) from the row histogram and appends
+//               the (key, position) of every score in bins >= b* to the row's
+//               candidate list (wave-aggregated atomics).
+//  4. final  -- one 1024-thread block per row: exact radix select of the k-th
+//               key inside bin b*, lower-position tie-break by a second
+//               radix select on positions, then the chosen positions are
+//               marked in an LDS bitmap and written out in ascending order.
+//               If the candidate list would overflow (scores concentrated
+//               in one bin) the block selects directly from the score row.
+#include "dsa_internal.h"
+#include "select.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kBins = 4096;     // top 12 bits of the order key
+constexpr int kBinShift = 20;
+constexpr int kSeg = 8192;      // scores per hist/gather block
+constexpr int kSegThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kMaxK = 4096;
+constexpr int kMaxS = 262144;
+
+__host__ __device__ inline size_t cap_for(int k) { return (size_t)2 * k + 4096; }
+__host__ __device__ inline size_t row_stride_bytes(int k) {
+  size_t b = (size_t)kBins * 4 + 256 + cap_for(k) * 8;
+  return (b + 255) & ~(size_t)255;
+}
+
+struct RowWs {
+  uint32_t* hist;   // [kBins]
+  uint32_t* meta;   // [64]: 0 = candidate count
+  uint32_t* ekey;   // [cap]
+  uint32_t* eidx;   // [cap]
+};
+
+__device__ __forceinline__ RowWs row_ws(void* ws, int r, int k) {
+  char* base = static_cast<char*>(ws) + (size_t)r * row_stride_bytes(k);
+  RowWs w;
+  w.hist = reinterpret_cast<uint32_t*>(base);
+  w.meta = reinterpret_cast<uint32_t*>(base + kBins * 4);
+  w.ekey = reinterpret_cast<uint32_t*>(base + kBins * 4 + 256);
+  w.eidx = w.ekey + cap_for(k);
+  return w;
+}
+
+__device__ __forceinline__ int row_valid_count(const TopkArgs& a, int r) {
+  const int pos = row_pos(a.seq_lens, a.row_begin + r, a.q_len, a.S_max);
+  return pos < 0 ? 0 : pos + 1;
+}
+
+__global__ void k_topk_zero(TopkArgs a) {
+  const size_t words = (size_t)kBins + 64;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words * a.row_count;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / words, j = i % words;
+    RowWs w = row_ws(a.ws, (int)r, a.k);
+    w.hist[j] = 0u;  // hist and meta are contiguous
+  }
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_topk_hist(TopkArgs a) {
+  __shared__ uint32_t h[kBins];
+  const int r = blockIdx.y;
+  const int n = row_valid_count(a, r);
+  const int seg0 = (int)blockIdx.x * kSeg;
+  if (n <= a.k || seg0 >= n) return;
+  for (int i = threadIdx.x; i < kBins; i += kSegThreads) h[i] = 0u;
+  __syncthreads();
+  const float* row = a.scores + (long long)r * a.ld;
+  const int e1 = min(seg0 + kSeg, n);
+  for (int e = seg0 + (int)threadIdx.x; e < e1; e += kSegThreads)
+    atomicAdd(&h[order_key(row[e]) >> kBinShift], 1u);
+  __syncthreads();
+  RowWs w = row_ws(a.ws, r, a.k);
+  for (int i = threadIdx.x; i < kBins; i += kSegThreads)
+    if (h[i]) atomicAdd(&w.hist[i], h[i]);
+}
+
+// Threshold bin: the bin b* with count(bins > b*) < k <= count(bins >= b*).
+// Threads walk the bins from the top; NT * per == kBins.
+template <int NT>
+__device__ void find_threshold_bin(const uint32_t* hist, uint32_t k, uint32_t* sm, uint32_t* out_bin,
+                                   uint32_t* out_above) {
+  constexpr int per = kBins / NT;
+  const int hi = kBins - per * (int)threadIdx.x;  // this thread owns bins [hi-per, hi)
+  uint32_t c[per];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    c[j] = hist[hi - 1 - j];
+    tot += c[j];
+  }
+  if (threadIdx.x == 0) {
+    sm[NT / 64 + 1] = 0u;
+    sm[NT / 64 + 2] = 0u;
+  }
+  uint32_t total;
+  const uint32_t above = block_exclusive_sum<NT>(tot, sm, &total);
+  if (above < k && k <= above + tot) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int j = 0; j < per; ++j) {
+      if (acc < k && k <= acc + c[j]) {
+        sm[NT / 64 + 1] = (uint32_t)(hi - 1 - j);
+        sm[NT / 64 + 2] = acc;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  *out_bin = sm[NT / 64 + 1];
+  *out_above = sm[NT / 64 + 2];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
+  __shared__ uint32_t sm[kSegThreads / 64 + 4];
+  const int r = blockIdx.y;
+  const int n = row_valid_count(a, r);
+  const int seg0 = (int)blockIdx.x * kSeg;
+  if (n <= a.k || seg0 >= n) return;
+  RowWs w = row_ws(a.ws, r, a.k);
+  uint32_t bstar, above;
+  find_threshold_bin<kSegThreads>(w.hist, (uint32_t)a.k, sm, &bstar, &above);
+  if ((size_t)above + w.hist[bstar] > cap_for(a.k)) return;  // final block takes the direct path
+  const float* row = a.scores + (long long)r * a.ld;
+  const int e1 = min(seg0 + kSeg, n);
+  const int lane = threadIdx.x & 63;
+  for (int e0 = seg0; e0 < e1; e0 += kSegThreads) {
+    const int e = e0 + (int)threadIdx.x;
+    uint32_t key = 0;
+    bool pred = false;
+    if (e < e1) {
+      key = order_key(row[e]);
+      pred = (key >> kBinShift) >= bstar;
+    }
+    const unsigned long long ball = __ballot(pred);
+    if (ball == 0ull) continue;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&w.meta[0], (uint32_t)__popcll(ball));
+    base = __shfl(base, 0, 64);
+    if (pred) {
+      const uint32_t slot = base + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
+      w.ekey[slot] = key;
+      w.eidx[slot] = (uint32_t)e;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
+  extern __shared__ uint32_t dyn[];
+  constexpr int NW = kFinThreads / 64;
+  uint32_t* whist = dyn;                 // NW * 256
+  uint32_t* sm = whist + NW * 256;       // 64
+  uint32_t* bitmap = sm + 64;            // ceil(S_max/32)
+  const int Wmax = (a.S_max + 31) >> 5;
+  uint32_t* skey = bitmap + Wmax;        // cap
+  uint32_t* sidx = skey + cap_for(a.k);  // cap
+
+  const int r = blockIdx.x;
+  const int n = row_valid_count(a, r);
+  int32_t* out = a.idx + (long long)r * a.k;
+  const int tid = threadIdx.x;
+  if (n <= a.k) {
+    for (int j = tid; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
+    return;
+  }
+  RowWs w = row_ws(a.ws, r, a.k);
+  uint32_t bstar, above;
+  find_threshold_bin<kFinThreads>(w.hist, (uint32_t)a.k, sm, &bstar, &above);
+  const uint32_t total = above + w.hist[bstar];
+  const bool direct = total > cap_for(a.k);
+  const float* row = a.scores + (long long)r * a.ld;
+
+  uint32_t tau, want, eq_total;
+  if (!direct) {
+    for (uint32_t i = tid; i < total; i += kFinThreads) {
+      skey[i] = w.ekey[i];
+      sidx[i] = w.eidx[i];
+    }
+    __syncthreads();
+    // Entries with bin > b* are all taken; resolve the rest inside bin b*.
+    tau = bstar << kBinShift;
+    want = (uint32_t)a.k - above;
+    radix_select_desc<kFinThreads>(
+        [&](auto f) {
+          for (uint32_t i = tid; i < total; i += kFinThreads) f(skey[i]);
+        },
+        tau, kBinShift, want, whist, sm);
+  } else {
+    tau = 0u;
+    want = (uint32_t)a.k;
+    radix_select_desc<kFinThreads>(
+        [&](auto f) {
+          for (int e = tid; e < n; e += kFinThreads) f(order_key(row[e]));
+        },
+        tau, 32, want, whist, sm);
+  }
+  // Count the copies of tau; if not all are taken, keep the `want` lowest
+  // positions among them (largest ~position first).
+  if (tid == 0) sm[8] = 0u;
+  __syncthreads();
+  {
+    uint32_t c = 0;
+    if (!direct) {
+      for (uint32_t i = tid; i < total; i += kFinThreads) c += (skey[i] == tau);
+    } else {
+      for (int e = tid; e < n; e += kFinThreads) c += (order_key(row[e]) == tau);
+    }
+    atomicAdd(&sm[8], c);
+  }
+  __syncthreads();
+  eq_total = sm[8];
+  __syncthreads();
+  uint32_t cut = 0xFFFFFFFFu;  // positions <= cut among the ties are taken
+  if (want < eq_total) {
+    uint32_t inv = 0u;
+    uint32_t wv = want;
+    if (!direct) {
+      radix_select_desc<kFinThreads>(
+          [&](auto f) {
+            for (uint32_t i = tid; i < total; i += kFinThreads)
+              if (skey[i] == tau) f(~sidx[i]);
+          },
+          inv, 32, wv, whist, sm);
+    } else {
+      radix_select_desc<kFinThreads>(
+          [&](auto f) {
+            for (int e = tid; e < n; e += kFinThreads)
+              if (order_key(row[e]) == tau) f(~(uint32_t)e);
+          },
+          inv, 32, wv, whist, sm);
+    }
+    cut = ~inv;
+  }
+  const int W = (n + 31) >> 5;
+  for (int i = tid; i < W; i += kFinThreads) bitmap[i] = 0u;
+  __syncthreads();
+  if (!direct) {
+    for (uint32_t i = tid; i < total; i += kFinThreads) {
+      const uint32_t key = skey[i], p = sidx[i];
+      if (key > tau || (key == tau && p <= cut)) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+    }
+  } else {
+    for (int e = tid; e < n; e += kFinThreads) {
+      const uint32_t key = order_key(row[e]);
+      if (key > tau || (key == tau && (uint32_t)e <= cut)) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+  const uint32_t written = min(bitmap_to_sorted<kFinThreads>(bitmap, n, out, (uint32_t)a.k, sm), (uint32_t)a.k);
+  for (int j = (int)written + tid; j < a.k; j += kFinThreads) out[j] = -1;
+}
+
+size_t final_lds_bytes(int S_max, int k) {
+  return ((size_t)(kFinThreads / 64) * 256 + 64 + ((S_max + 31) >> 5) + 2 * cap_for(k)) * 4;
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int row_count, int S_max, int k) {
+  (void)S_max;
+  if (row_count <= 0 || k <= 0) return 0;
+  return (size_t)row_count * row_stride_bytes(k);
+}
+
+bool topk_supported(int S_max, int k) {
+  return k >= 1 && k <= kMaxK && S_max >= 1 && S_max <= kMaxS && final_lds_bytes(S_max, k) <= 160 * 1024;
+}
+
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
+  if (a.row_count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
+  const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);
+  hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
+  hipLaunchKernelGGL(k_topk_gather, segs, dim3(kSegThreads), 0, stream, a);
+  const size_t lds = final_lds_bytes(a.S_max, a.k);
+  hipLaunchKernelGGL(k_topk_final, dim3((unsigned)a.row_count), dim3(kFinThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,99 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/dsa.h declares, and its host-side validation rejects bad arguments
+before anything is enqueued (no device is touched by these calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_lightning_amd as lcl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"DSA_API\s+[\w\s\*]+?\b(dsa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = _declared()
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla", "dsa_forward"):
+        assert fn in names
+    assert set(names) == set(lcl.ABI_FUNCTIONS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = lcl.load()
+    for fn in _declared():
+        assert hasattr(lib, fn), fn
+    assert lib.dsa_version().decode().count(".") == 2
+    for code in range(5):
+        assert lib.dsa_status_string(code)
+
+
+def _geom(B=1, q_len=1, S=16, seq=0x1000):
+    return lcl.Geom(B, q_len, S, seq)
+
+
+FAKE = 0x10000  # a 256-aligned non-null address; never dereferenced: validation fails first
+
+
+def test_indexer_validation():
+    lib = lcl.load()
+    g = _geom()
+    P = ctypes.c_void_p
+    call = lambda geom, q, qd, w, wd, k, kd, rb, rc, sc, ld: lib.dsa_indexer_scores(
+        geom, P(q), qd, None, P(w), wd, P(k), kd, None, rb, rc, P(sc), ld, None)
+    assert call(None, FAKE, 2, FAKE, 1, FAKE, 2, 0, 1, FAKE, 16) == 1              # no geometry
+    assert call(ctypes.byref(g), 0, 2, FAKE, 1, FAKE, 2, 0, 1, FAKE, 16) == 1      # null q
+    assert call(ctypes.byref(g), FAKE + 8, 2, FAKE, 1, FAKE, 2, 0, 1, FAKE, 16) == 1  # misaligned q
+    assert call(ctypes.byref(g), FAKE, 2, FAKE, 1, FAKE, 0, 0, 1, FAKE, 16) == 2   # q fp8, k f32
+    assert call(ctypes.byref(g), FAKE, 0, FAKE, 1, FAKE, 0, 0, 1, FAKE, 16) == 2   # f32 q with bf16 w
+    assert call(ctypes.byref(g), FAKE, 2, FAKE, 1, FAKE, 2, 0, 2, FAKE, 16) == 1   # rows beyond T
+    assert call(ctypes.byref(g), FAKE, 2, FAKE, 1, FAKE, 2, 0, 1, FAKE, 15) == 1   # ld < S_max
+    bad = _geom(B=1, q_len=20, S=16)
+    assert call(ctypes.byref(bad), FAKE, 2, FAKE, 1, FAKE, 2, 0, 1, FAKE, 16) == 1  # q_len > S_max
+    assert call(ctypes.byref(g), FAKE, 2, FAKE, 1, FAKE, 2, 0, 0, FAKE, 16) == 0   # nothing to do
+
+
+def test_topk_validation_and_workspace():
+    lib = lcl.load()
+    g = _geom(B=2, q_len=1, S=5000)
+    P = ctypes.c_void_p
+    need = lib.dsa_topk_workspace_size(2, 5000, 256)
+    assert need > 0
+    assert lib.dsa_topk(ctypes.byref(g), P(FAKE), 5000, 0, 2, 0, P(FAKE), P(FAKE), need, None) == 1   # k = 0
+    assert lib.dsa_topk(ctypes.byref(g), P(FAKE), 5000, 0, 2, 8192, P(FAKE), P(FAKE), 1 << 30, None) == 2  # k too big
+    assert lib.dsa_topk(ctypes.byref(g), P(FAKE), 5000, 0, 2, 256, P(FAKE), P(FAKE), need - 1, None) == 3
+    assert lib.dsa_topk(ctypes.byref(g), P(FAKE), 5000, 0, 2, 256, P(FAKE), P(FAKE + 16), need, None) == 3
+    big = _geom(B=1, q_len=1, S=1 << 20)
+    assert lib.dsa_topk(ctypes.byref(big), P(FAKE), 1 << 20, 0, 1, 256, P(FAKE), P(FAKE), 1 << 30, None) == 2
+
+
+def test_sparse_mla_validation():
+    lib = lcl.load()
+    g = _geom(B=1, q_len=2, S=100)
+    P = ctypes.c_void_p
+    call = lambda H, k, dt, ws, wsb: lib.dsa_sparse_mla(ctypes.byref(g), H, k, 0.1, P(FAKE), dt, P(FAKE), P(FAKE),
+                                                        P(FAKE), None, P(ws), wsb, None)
+    assert call(24, 64, 1, FAKE, 1 << 30) == 2      # bf16 needs H % 16 == 0
+    assert call(0, 64, 1, FAKE, 1 << 30) == 1
+    assert call(16, 0, 1, FAKE, 1 << 30) == 1
+    assert call(16, 64, 2, FAKE, 1 << 30) == 2      # fp8 attention not offered
+    assert call(16, 20000, 0, FAKE, 1 << 30) == 1   # k beyond the limit
+    need = lib.dsa_sparse_mla_workspace_size(1, 2, 128, 2048, 1)
+    assert need > 0                                 # two query rows: split partials
+    assert call(128, 2048, 1, FAKE, need - 1) == 3
+
+
+def test_forward_workspace_sizes_are_consistent():
+    lib = lcl.load()
+    dec = lib.dsa_forward_workspace_size(16, 2, 131072, 128, 2048, 2, 1)
+    assert dec >= 32 * 131072 * 4               # materialised decode scores
+    pre = lib.dsa_forward_workspace_size(1, 65536, 65536, 128, 2048, 2, 1)
+    assert pre < 65536 * 65536 * 4 // 4         # streaming prefill never holds T x S
+    assert lib.dsa_forward_workspace_size(0, 1, 1, 1, 1, 2, 1) == 0

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances: indexer scores within 2e-2 relative; top-k sets identical outside
+a 1e-3-relative band around the k-th score (and bit-exact when dsa_topk runs on
+the GPU's own scores); attention outputs within 1e-2 max-abs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import query_positions, topk_select
+from synth import baseline_workload, make_workload
+from tests.gpu_util import Uploaded, check_attention, check_scores, check_topk, from_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+SMALL = [
+    # name, B, q_len, seq_lens, S_max, topk, H, fp8, ki_mode
+    ("decode_ragged", 3, 1, [3000, 1777, 2049], 3000, 256, 32, True, "normal"),
+    ("decode_two_q", 4, 2, [5000, 4095, 4097, 300], 5000, 512, 16, True, "normal"),
+    ("decode_ties", 2, 2, [6000, 5001], 6000, 256, 16, True, "pool"),
+    ("prefill_small", 1, 700, [700], 700, 128, 16, True, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_indexer_and_topk_small(dsa_gpu, case):
+    name, B, q_len, seq, S, k, H, fp8, mode = case
+    _say(f"[indexer+topk] {name}")
+    wl = make_workload(name, B, q_len, seq, S, k, H, fp8=fp8, seed=11, ki_mode=mode)
+    up = Uploaded(wl, with_mla=False)
+    g = up.geom(dsa_gpu)
+    sc = dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki, k_scale=up.d_ks)
+    idx = dsa_gpu.topk(g, sc, k)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    ref = up.oracle_scores()
+    pos = wl.positions()
+    check_scores(got, ref, pos)
+    check_topk(idx.cpu().numpy(), ref, pos, k)
+    # standalone top-k on the GPU's own scores must equal the oracle rule bit-exactly
+    gi = idx.cpu().numpy()
+    for r in range(wl.T):
+        want, _ = topk_select(got[r].astype(np.float64), pos[r], k)
+        assert np.array_equal(gi[r], want), f"row {r}: dsa_topk differs from the selection rule on its own scores"
+
+
+def test_indexer_row_slice_and_ld(dsa_gpu):
+    _say("[indexer] row slice with padded ld")
+    wl = make_workload("slice", 2, 40, [3000, 2500], 3000, 64, 16, seed=12)
+    up = Uploaded(wl, with_mla=False)
+    g = up.geom(dsa_gpu)
+    ld = 3008
+    buf = torch.full((30, ld), 7.0, device="cuda")
+    dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki, k_scale=up.d_ks, row_begin=25, row_count=30, scores=buf)
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    rows = np.arange(25, 55)
+    ref = up.oracle_scores(rows=rows)
+    check_scores(got[:, :3000], ref, wl.positions()[rows])
+    assert np.all(got[:, 3000:] == 7.0), "columns beyond S_max must be untouched"
+
+
+def test_topk_synthetic_ties_and_short_rows(dsa_gpu):
+    _say("[topk] synthetic ties / short rows / concentrated rows")
+    rng = np.random.default_rng(5)
+    B, q_len, S = 6, 1, 20000
+    seq = np.array([20000, 17, 20000, 20000, 9000, 2049], np.int32)
+    scores = rng.integers(-5, 6, (B, S)).astype(np.float32)          # massive ties
+    scores[2] = 1.0                                                    # one value everywhere
+    scores[3] = (1.0 + rng.standard_normal(S) * 1e-6).astype(np.float32)  # all in one bin
+    scores[4] = rng.standard_normal(S).astype(np.float32)
+    d_seq = torch.from_numpy(seq).cuda()
+    g = dsa_gpu.make_geom(B, q_len, S, d_seq)
+    for k in (1, 7, 2048, 4096):
+        idx = dsa_gpu.topk(g, torch.from_numpy(scores).cuda(), k).cpu().numpy()
+        for r in range(B):
+            want, _ = topk_select(scores[r].astype(np.float64), seq[r] - 1, k)
+            assert np.array_equal(idx[r], want), f"k={k} row {r}"
+
+
+MLA_CASES = [
+    # name, B, q_len, seq_lens, S_max, k, H, bf16
+    ("decode_bf16", 3, 2, [5000, 3000, 2], 5000, 512, 128, True),
+    ("decode_bf16_h32", 2, 1, [4000, 100], 4000, 300, 32, True),
+    ("prefill_bf16", 1, 96, [1000], 1000, 256, 64, True),
+    ("tiny_f32", 1, 64, [200], 200, 64, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_sparse_mla(dsa_gpu, case):
+    name, B, q_len, seq, S, k, H, bf16 = case
+    _say(f"[sparse_mla] {name}")
+    wl = make_workload(name, B, q_len, seq, S, k, H, fp8=bf16, seed=13)
+    up = Uploaded(wl)
+    rng = np.random.default_rng(3)
+    pos = wl.positions()
+    idx = np.full((wl.T, k), -1, np.int32)
+    for t in range(wl.T):
+        n = min(k, pos[t] + 1) - (t % 3)  # some rows not full
+        if n > 0:
+            idx[t, :n] = rng.choice(pos[t] + 1, n, replace=False)
+        rng.shuffle(idx[t])
+    out, lse = dsa_gpu.sparse_mla(up.geom(dsa_gpu), up.d_qm, up.d_kv, to_dev(idx), wl.sm_scale)
+    torch.cuda.synchronize()
+    check_attention(from_dev(out), lse.cpu().numpy(), up, idx.astype(np.int64), np.arange(wl.T))
+
+
+FWD_CASES = [
+    ("fwd_decode", 4, 2, [6000, 3001, 4500, 2048], 6000, 512, 32, "normal"),
+    ("fwd_decode_ties", 2, 2, [7000, 7000], 7000, 512, 16, "pool"),
+    ("fwd_prefill_stream", 1, 1500, [1500], 1500, 256, 16, "normal"),
+    ("fwd_prefill_stream_b2", 2, 200, [2600, 300], 2600, 128, 16, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_forward(dsa_gpu, case):
+    name, B, q_len, seq, S, k, H, mode = case
+    _say(f"[forward] {name}")
+    wl = make_workload(name, B, q_len, seq, S, k, H, seed=14, ki_mode=mode)
+    up = Uploaded(wl)
+    g = up.geom(dsa_gpu)
+    idx, out, lse = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                    index_k_scale=up.d_ks)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    ref = up.oracle_scores()
+    pos = wl.positions()
+    check_topk(gi, ref, pos, k)
+    check_attention(from_dev(out), lse.cpu().numpy(), up, gi.astype(np.int64), np.arange(wl.T))
+
+
+# ---------------------------------------------------------------- full sizes
+
+def test_full_tiny512(dsa_gpu):
+    _say("[full] tiny512 (fp32 throughout)")
+    wl = baseline_workload("tiny512")
+    up = Uploaded(wl)
+    g = up.geom(dsa_gpu)
+    sc = dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki)
+    idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv)
+    torch.cuda.synchronize()
+    ref = up.oracle_scores()
+    pos = wl.positions()
+    check_scores(sc.cpu().numpy(), ref, pos)
+    gi = idx.cpu().numpy()
+    check_topk(gi, ref, pos, wl.topk)
+    check_attention(out.cpu().numpy().astype(np.float64), lse.cpu().numpy(), up, gi.astype(np.int64),
+                    np.arange(wl.T))
+
+
+@pytest.mark.parametrize("name", ["decode32k", "decode128k"])
+def test_full_decode(dsa_gpu, name):
+    _say(f"[full] {name}")
+    wl = baseline_workload(name)
+    up = Uploaded(wl)
+    g = up.geom(dsa_gpu)
+    idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                    index_k_scale=up.d_ks)
+    sc = dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki, k_scale=up.d_ks)
+    torch.cuda.synchronize()
+    ref = up.oracle_scores()
+    pos = wl.positions()
+    got = sc.cpu().numpy()
+    check_scores(got, ref, pos)
+    gi = idx.cpu().numpy()
+    check_topk(gi, ref, pos, wl.topk)
+    for r in range(wl.T):  # the forward's selection is the rule applied to the GPU's own scores
+        want, _ = topk_select(got[r].astype(np.float64), pos[r], wl.topk)
+        assert np.array_equal(gi[r], want), f"row {r}"
+    check_attention(from_dev(out), lse.cpu().numpy(), up, gi.astype(np.int64), np.arange(wl.T))
+
+
+def test_full_prefill8k_planted(dsa_gpu):
+    _say("[full] prefill8k planted (streaming path)")
+    wl = baseline_workload("prefill8k")
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([wl.planted_rows, [0, 1, 2046, 2047, 2048, 2049, 8191],
+                                       rng.choice(8192, 24, replace=False)]))
+    up = Uploaded(wl, qm_rows=sample)
+    g = up.geom(dsa_gpu)
+    idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                    index_k_scale=up.d_ks)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    for t in wl.planted_rows:
+        assert np.array_equal(gi[t], wl.planted_set), f"planted row {t} lost its planted set"
+    ref = up.oracle_scores(rows=sample)
+    check_topk(gi[sample], ref, wl.positions()[sample], wl.topk)
+    check_attention(from_dev(out)[sample], lse.cpu().numpy()[sample], up, gi[sample].astype(np.int64), sample)
+
+
+def test_full_prefill64k_sampled(dsa_gpu):
+    _say("[full] prefill64k sampled rows (streaming path)")
+    wl = baseline_workload("prefill64k")
+    rng = np.random.default_rng(2)
+    k = wl.topk
+    sample = np.unique(np.concatenate([[0, 1, 2, k - 2, k - 1, k, k + 1], np.arange(65536 - 8, 65536),
+                                       rng.choice(65536, 12, replace=False)]))
+    up = Uploaded(wl, qm_rows=sample)
+    g = up.geom(dsa_gpu)
+    idx, out, lse = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                    index_k_scale=up.d_ks, want_lse=True)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()[sample]
+    ref = up.oracle_scores(rows=sample)
+    check_topk(gi, ref, wl.positions()[sample], k)
+    check_attention(from_dev(out[torch.from_numpy(sample).cuda()]), lse.cpu().numpy()[sample], up,
+                    gi.astype(np.int64), sample)
