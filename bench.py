@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA forward path (indexer -> top-k -> sparse MQA-MLA) on
+one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-prefill] [--no-cpu-baseline]
+
+One step = one dsa_forward over one batch of the 128K-context decode workload
+(16 sequences x 2 new queries, context 131072, indexer 64x128 fp8 with
+per-token scales, top-k 2048, 128-head sparse MLA over the bf16 576-wide
+latent cache).  Inputs are seeded synthetic data resident in HBM before the
+timed region.  Before every step a 512 MiB buffer is overwritten so the
+256 MiB last-level cache does not hold the previous step's caches; each step
+is timed with HIP events on the launch stream and ms_per_step is their mean.
+
+Prints ONE JSON line with the headline decode throughput, per-stage timings
+and roofline fractions, the 64K-token prefill throughput, and the float64
+CPU oracle timed on a bounded sample of the decode workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scrub", action="store_true", help="do not evict the last-level cache between steps")
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the work; --gpus {args.gpus} is not supported "
+              f"(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import long_context_lightning_amd as lcl
+    from synth import baseline_workload
+
+    lcl.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------ decode 128K
+    wl = baseline_workload("decode128k")
+    log(f"generating {wl.name}: B={wl.B} q_len={wl.q_len} S={wl.S_max} k={wl.topk} H={wl.H}")
+    t0 = time.time()
+    qi, w = wl.qi(), wl.w()
+    ki, ks = wl.ki_all()
+    qm = wl.qm()
+    kv = wl.kv_all()
+    log(f"generated in {time.time() - t0:.1f}s; uploading")
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    d = dict(qi=up(qi), w=up(w), ki=up(ki), ks=up(ks), qm=up(qm), kv=up(kv),
+             seq=torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev))
+    del kv
+    geom = lcl.make_geom(wl.B, wl.q_len, wl.S_max, d["seq"])
+    T, k, H = wl.T, wl.topk, wl.H
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(lcl.forward_workspace_size(wl.B, wl.q_len, wl.S_max, H, k, lcl.FP8_E4M3FN, lcl.BF16),
+                     dtype=torch.uint8, device=dev)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def forward():
+        lcl.forward(geom, k, wl.sm_scale, d["qi"], d["w"], d["ki"], d["qm"], d["kv"], index_k_scale=d["ks"],
+                    idx=idx, out=out, lse=lse, ws=ws)
+
+    def evict():
+        if not args.no_scrub:
+            scrub.fill_(1)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        evict()
+        forward()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        evict()
+        ev[i][0].record(stream)
+        forward()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    ms = sum(step_ms) / len(step_ms)
+    value = T / (ms / 1e3)
+    log(f"decode forward: {ms * 1e3:.1f} us/step -> {value:,.0f} queries/s (wall {wall:.3f}s incl. scrubs)")
+
+    # Per-stage timing: the same kernels through the three stage calls.
+    scores = ws[: T * wl.S_max * 4].view(torch.float32).view(T, wl.S_max)
+    tk_ws = torch.empty(max(lcl.topk_workspace_size(T, wl.S_max, k), 256), dtype=torch.uint8, device=dev)
+    mla_ws = torch.empty(max(lcl.sparse_mla_workspace_size(wl.B, wl.q_len, H, k, lcl.BF16), 256),
+                         dtype=torch.uint8, device=dev)
+    st = {n: [] for n in ("indexer", "topk", "sparse_mla")}
+    for i in range(args.warmup + args.steps):
+        evict()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        lcl.indexer_scores(geom, d["qi"], d["w"], d["ki"], k_scale=d["ks"], scores=scores)
+        e[1].record(stream)
+        lcl.topk(geom, scores, k, idx=idx, ws=tk_ws)
+        e[2].record(stream)
+        lcl.sparse_mla(geom, d["qm"], d["kv"], idx, wl.sm_scale, out=out, lse=lse, ws=mla_ws)
+        e[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            st["indexer"].append(e[0].elapsed_time(e[1]))
+            st["topk"].append(e[1].elapsed_time(e[2]))
+            st["sparse_mla"].append(e[2].elapsed_time(e[3]))
+    st_ms = {n: sum(v) / len(v) for n, v in st.items()}
+    # algorithmic bytes per launch (decode is HBM-bound)
+    idx_bytes = wl.B * wl.S_max * (128 + 4)
+    topk_bytes = T * wl.S_max * 4
+    mla_bytes = T * k * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * k * 4
+    stage_bytes = {"indexer": idx_bytes, "topk": topk_bytes, "sparse_mla": mla_bytes}
+    stages = {}
+    for n in st_ms:
+        gbs = stage_bytes[n] / (st_ms[n] * 1e-3) / 1e9
+        stages[n] = {"us": round(st_ms[n] * 1e3, 2), "bytes": stage_bytes[n], "GB_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"  {n:10s} {st_ms[n] * 1e3:8.1f} us  {gbs:8.1f} GB/s  ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+    dom = max(st_ms, key=st_ms.get)
+    dom_gbs = stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    del scores
+
+    # --------------------------------------------------------- prefill 64K
+    prefill = None
+    if not args.no_prefill:
+        del d, idx, out, lse, ws, tk_ws, mla_ws
+        torch.cuda.empty_cache()
+        prefill = bench_prefill(args, lcl, torch, np, dev, stream, evict)
+
+    # ------------------------------------------------------ CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, qi, w, ki, ks, qm, np)
+
+    line = {
+        "metric": "DSA decode queries/s @128K ctx (dsa_forward: indexer + top-k + sparse MLA)",
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 indexer / fp32 accumulate / bf16 attention",
+        "data": "synthetic (seeded; shapes and distributions of the 128K decode workload)",
+        "config": {"workload": "decode128k: 16 seqs x 2 queries, ctx 131072, indexer 64x128 fp8, top-k 2048, "
+                               "128-head MQA-MLA bf16 576/512",
+                   "batch_queries": T, "context": wl.S_max, "topk": k, "heads": H,
+                   "llc_scrub_between_steps": not args.no_scrub},
+        "roofline": roofline,
+        "stages": stages,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_prefill(args, lcl, torch, np, dev, stream, evict):
+    """64K-token causal prefill; inputs drawn on the GPU with torch's seeded
+    generator following the same recipe (q, k ~ N(0,1) -> e4m3 with per-token
+    k scales, w ~ N(0,1)/8 bf16, MLA q and cache ~ N(0,1) bf16)."""
+    L, k, H = 65536, 2048, 128
+    log(f"prefill: L={L} k={k} H={H}; drawing inputs on the GPU")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    qi = torch.randn((L, 64, 128), generator=gen, device=dev).to(torch.float8_e4m3fn)
+    kf = torch.randn((1, L, 128), generator=gen, device=dev)
+    ks = (kf.abs().amax(dim=-1).clamp_min(2.0 ** -126) / 448.0).float()
+    ki = (kf / ks[..., None]).to(torch.float8_e4m3fn)
+    del kf
+    w = (torch.randn((L, 64), generator=gen, device=dev) / 8).to(torch.bfloat16)
+    qm = torch.empty((L, H, 576), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, L, 4096):
+        qm[r0:r0 + 4096] = torch.randn((4096, H, 576), generator=gen, device=dev).to(torch.bfloat16)
+    kv = torch.randn((1, L, 576), generator=gen, device=dev).to(torch.bfloat16)
+    seq = torch.tensor([L], dtype=torch.int32, device=dev)
+    geom = lcl.make_geom(1, L, L, seq)
+    idx = torch.empty((L, k), dtype=torch.int32, device=dev)
+    out = torch.empty((L, H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lcl.forward_workspace_size(1, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16), dtype=torch.uint8,
+                     device=dev)
+    mla_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(192.0)
+    fwd_ms, mla_ms = [], []
+    n = args.prefill_steps
+    for i in range(1 + n):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        evict()
+        e[0].record(stream)
+        lcl.forward(geom, k, sm, qi, w, ki, qm, kv, index_k_scale=ks, idx=idx, out=out, ws=ws, want_lse=False)
+        e[1].record(stream)
+        lcl.sparse_mla(geom, qm, kv, idx, sm, out=out, ws=mla_ws, want_lse=False)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= 1:
+            fwd_ms.append(e[0].elapsed_time(e[1]))
+            mla_ms.append(e[1].elapsed_time(e[2]))
+        log(f"prefill step {i}: forward {e[0].elapsed_time(e[1]):.2f} ms, sparse MLA alone {e[1].elapsed_time(e[2]):.2f} ms")
+    f_ms = sum(fwd_ms) / len(fwd_ms)
+    m_ms = sum(mla_ms) / len(mla_ms)
+    i_ms = max(f_ms - m_ms, 1e-6)
+    pairs = L * (L + 1) // 2
+    idx_tflops = pairs * 64 * 128 * 2 / (i_ms * 1e-3) / 1e12
+    sel_rows = sum(min(t + 1, k) for t in range(L))
+    mla_tflops = sel_rows * H * (576 + 512) * 2 / (m_ms * 1e-3) / 1e12
+    log(f"prefill: {L / (f_ms * 1e-3):,.0f} tokens/s; indexer+top-k {i_ms:.2f} ms = {idx_tflops:.0f} TFLOP/s "
+        f"({idx_tflops / FP8_PEAK_TFLOPS:.1%} fp8 peak); sparse MLA {m_ms:.2f} ms = {mla_tflops:.0f} TFLOP/s "
+        f"({mla_tflops / BF16_PEAK_TFLOPS:.1%} bf16 peak)")
+    res = {"workload": "prefill64k: 1 x 65536 causal, indexer fp8 64x128, top-k 2048, 128-head MQA-MLA bf16",
+           "tokens_per_s": round(L / (f_ms * 1e-3), 1), "ms_per_step": round(f_ms, 3), "steps": n,
+           "indexer_topk_ms": round(i_ms, 3), "indexer_tflops": round(idx_tflops, 1),
+           "indexer_fp8_mfma_frac": round(idx_tflops / FP8_PEAK_TFLOPS, 4),
+           "sparse_mla_ms": round(m_ms, 3), "sparse_mla_tflops": round(mla_tflops, 1),
+           "sparse_mla_bf16_mfma_frac": round(mla_tflops / BF16_PEAK_TFLOPS, 4),
+           "data": "synthetic, drawn on the GPU with torch's seeded generator (same recipe)"}
+    del qi, ki, ks, w, qm, kv, idx, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, qi, w, ki, ks, qm, np):
+    """The float64 oracle on a bounded sample: the queries of the first
+    sequences of the decode workload, through all three stages."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    nseq = 2
+    rows = np.arange(nseq * wl.q_len)
+    log(f"cpu baseline: oracle on {len(rows)} decode queries ({nseq} sequences), {cores} cores")
+    kv = np.stack([wl.kv(b) for b in range(nseq)] + [np.zeros((1, 576), np.uint16)] * 0)
+    t0 = time.perf_counter()
+    seq = wl.seq_lens[:nseq]
+    oracle.dsa_forward(qi[rows], "e4m3fn", w[rows], "bf16", ki[:nseq], "e4m3fn", qm[rows], "bf16", kv, "bf16",
+                       seq, wl.q_len, wl.topk, wl.sm_scale, k_scale=ks[:nseq])
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {dt:.1f}s for {len(rows)} queries")
+    return {"value": round(len(rows) / dt, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(rows)} queries ({nseq} sequences x {wl.q_len}) of the 128K decode workload, "
+                      f"all three stages in float64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

@@ -2,8 +2,10 @@
 //
 //   I[t,s] = k_scale[s] * sum_j w[t,j]*q_scale[t,j] * ReLU(q[t,j,:] . k[s,:])
 //
-// fp8 path: one wave owns 64 consecutive keys of one sequence and up to NQ
-// query rows of that sequence.  The 64x128 query tile of a row stays in
+// fp8 path: a block owns a 2048-key chunk of one sequence and up to NQ query
+// rows of that sequence; its four waves step through the chunk 64 keys each
+// per step, with the next step's key fragments loaded while the current step
+// computes.  The 64x128 query tile of a row stays in
 // registers as four A fragments of v_mfma_f32_16x16x128_f8f6f4 (16 heads x
 // the full 128-deep dot each), each 16-key block of the fp8 key cache is
 // loaded straight from HBM into a B fragment (four lanes per 128-byte key
@@ -20,8 +22,9 @@ namespace dsa {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
-constexpr int kKeysPerWave = 64;
-constexpr int kKeysPerBlock = kWavesPerBlock * kKeysPerWave;
+constexpr int kKeysPerWave = 64;                               // keys per wave per step
+constexpr int kKeysPerBlock = kWavesPerBlock * kKeysPerWave;   // keys per block per step
+constexpr int kKeysPerChunk = 2048;                            // keys streamed by one block
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   v4i lo = *reinterpret_cast<const v4i*>(p);
@@ -54,7 +57,7 @@ __device__ __forceinline__ RowGroup row_group(const IndexerArgs& a) {
 }
 
 template <int NQ, bool WBF16>
-__global__ __launch_bounds__(256) void k_indexer_fp8(IndexerArgs a) {
+__global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -67,25 +70,34 @@ __global__ __launch_bounds__(256) void k_indexer_fp8(IndexerArgs a) {
   for (int r = 0; r < NQ; ++r) pos[r] = (r < rg.nr) ? L - a.q_len + qi0 + r : -1;
   const int maxpos = L - a.q_len + qi0 + rg.nr - 1;
 
-  const int kw = (int)blockIdx.x * kKeysPerBlock + wave * kKeysPerWave;
-  if (kw >= a.S_max) return;
-  const int s_l = kw + lane;  // key whose finished score this lane stores
+  // This block streams keys [chunk0, chunk1); the four waves interleave
+  // 64-key steps so the block reads one contiguous region at a time.
+  const int chunk0 = (int)blockIdx.x * kKeysPerChunk;
+  const int chunk1 = min(chunk0 + kKeysPerChunk, a.S_max);
+  const int kend = min(chunk1, maxpos + 1);  // keys past this are masked for every row
   float* out = a.scores + (long long)(rg.t0 - a.row_begin) * a.ld;
-  if (kw > maxpos) {  // the whole wave is beyond every row's position
-    if (s_l < a.S_max)
-      for (int r = 0; r < rg.nr; ++r) out[(long long)r * a.ld + s_l] = -INFINITY;
-    return;
-  }
 
-  // Key fragments first so the HBM stream starts as early as possible.
+  // Fully masked tail of the chunk: -inf, no scoring.
+  for (int s = max(chunk0, kend) + (int)threadIdx.x; s < chunk1; s += 256)
+    for (int r = 0; r < rg.nr; ++r) out[(long long)r * a.ld + s] = -INFINITY;
+  if (kend <= chunk0) return;
+  const int nsteps = (kend - chunk0 + kKeysPerBlock - 1) / kKeysPerBlock;
+
   const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
-  v8i kf[4];
+  const float* ksb = a.k_scale ? a.k_scale + (size_t)rg.b * a.S_max : nullptr;
+  auto load_keys = [&](int step, v8i (&kf)[4], float& ks) {
+    const int kw = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    const int s = kw + 16 * blk + c;
-    kf[blk] = (s < a.S_max) ? load32(kb + (size_t)s * kDI + 32 * g) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  const float ks = (a.k_scale && s_l < a.S_max) ? a.k_scale[(size_t)rg.b * a.S_max + s_l] : 1.0f;
+    for (int blk = 0; blk < 4; ++blk) {
+      const int s = kw + 16 * blk + c;
+      kf[blk] = (s < kend) ? load32(kb + (size_t)s * kDI + 32 * g) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    const int s_l = kw + lane;
+    ks = (ksb && s_l < kend) ? ksb[s_l] : 1.0f;
+  };
+  v8i kf_cur[4], kf_nxt[4];
+  float ks_cur, ks_nxt;
+  load_keys(0, kf_cur, ks_cur);
 
   // Query fragments (row = head 16m+c, bytes 32g..32g+31) and head weights of
   // the output rows this lane holds (heads 16m + 4g + i).
@@ -118,34 +130,41 @@ __global__ __launch_bounds__(256) void k_indexer_fp8(IndexerArgs a) {
     }
   }
 
-  float x[NQ][4];
+  for (int step = 0; step < nsteps; ++step) {
+    if (step + 1 < nsteps) load_keys(step + 1, kf_nxt, ks_nxt);
+    const int s_l = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave + lane;
+    float x[NQ][4];
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+      for (int r = 0; r < NQ; ++r) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const v4f d = mfma_fp8_16x16x128(qf[r][m], kf_cur[blk]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], fmaxf(d[i], 0.f), acc);
+        }
+        x[r][blk] = acc;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < NQ; ++r) {
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const v4f d = mfma_fp8_16x16x128(qf[r][m], kf[blk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], fmaxf(d[i], 0.f), acc);
-      }
-      x[r][blk] = acc;
+      // Transpose-reduce over the four 16-lane rows: afterwards lane (g, c)
+      // holds the head sum of block g, key column c, i.e. key s_l.
+      auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][0]), __float_as_uint(x[r][1]), false, false);
+      auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][2]), __float_as_uint(x[r][3]), false, false);
+      const float a01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
+      const float a23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
+      auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
+      const float tot = __uint_as_float(pf[0]) + __uint_as_float(pf[1]);
+      if (r < rg.nr && s_l < kend) out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? tot * ks_cur : -INFINITY;
     }
-  }
-
+    if (step + 1 < nsteps) {
 #pragma unroll
-  for (int r = 0; r < NQ; ++r) {
-    // Transpose-reduce over the four 16-lane rows: afterwards lane (g, c)
-    // holds the head sum of block g, key column c, i.e. key kw + lane.
-    auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][0]), __float_as_uint(x[r][1]), false, false);
-    auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r][2]), __float_as_uint(x[r][3]), false, false);
-    const float a01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
-    const float a23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
-    auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
-    const float tot = __uint_as_float(pf[0]) + __uint_as_float(pf[1]);
-    if (r < rg.nr && s_l < a.S_max)
-      out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? tot * ks : -INFINITY;
+      for (int blk = 0; blk < 4; ++blk) kf_cur[blk] = kf_nxt[blk];
+      ks_cur = ks_nxt;
+    }
   }
 }
 
@@ -203,7 +222,7 @@ hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t stream) {
   const int b0 = a.row_begin / a.q_len;
   const int b1 = (a.row_begin + a.row_count - 1) / a.q_len;
   const dim3 block(256);
-  const unsigned gx = (unsigned)((a.S_max + kKeysPerBlock - 1) / kKeysPerBlock);
+  const unsigned gx = (unsigned)((a.S_max + kKeysPerChunk - 1) / kKeysPerChunk);
   if (a.q_len == 1) {
     const dim3 grid(gx, (unsigned)(b1 - b0 + 1));
     if (a.w_is_bf16) hipLaunchKernelGGL((k_indexer_fp8<1, true>), grid, block, 0, stream, a);

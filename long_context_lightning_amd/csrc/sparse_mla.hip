@@ -29,22 +29,44 @@ namespace dsa {
 
 namespace {
 
-constexpr int kNT = 32;                 // keys per tile
-constexpr int kRowBytes = kDQK * 2;     // 1152
-constexpr int kRS = kRowBytes + 16;     // padded LDS row stride (bank spread)
-constexpr int kPieces = kNT * (kRowBytes / 16);  // 16-byte pieces per tile (2304)
-constexpr int kThreads = 512;
-constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;  // 5
+constexpr int kNT = 32;                          // keys per tile
+constexpr int kRowBytes = kDQK * 2;              // 1152
+constexpr int kSlots = kRowBytes / 16 + 1;       // 72 data slots + 1 pad slot per LDS row
+constexpr int kRS = kSlots * 16;                 // 1168-byte LDS row stride
+constexpr int kTileBytes = kNT * kRS;            // 37376
+constexpr int kWaves = 4;                        // 32 heads per wave -> up to 128 heads
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = kNT / kWaves;       // rows of a tile gathered by each wave
+constexpr int kWaveSlots = kRowsPerWave * kSlots;
+constexpr int kDma = (kWaveSlots + 63) / 64;     // gather instructions per wave per tile (10)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
+
+// Wait until at most n of this wave's vector-memory operations are in flight.
+__device__ __forceinline__ void vm_wait(int n) {
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  if (n >= 2 * kDma)
+    __builtin_amdgcn_s_waitcnt(((2 * kDma) & 15) | (((2 * kDma) >> 4) << 14) | 0x70 | 0xF00);
+  else if (n >= kDma)
+    __builtin_amdgcn_s_waitcnt((kDma & 15) | ((kDma >> 4) << 14) | 0x70 | 0xF00);
+  else
+    __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+}
+
+// Block barrier for the gather ring: LDS writes of this wave done (lgkmcnt),
+// then s_barrier.  Unlike __syncthreads() it does not drain the vector-memory
+// counter, so the gathers of later tiles stay in flight across it; each wave
+// has already waited (vm_wait) for its own share of the tile being released.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Partition of one row's k indices into splits of whole tiles.
 __host__ __device__ inline int mla_splits(int T, int k) {
@@ -61,196 +83,272 @@ __host__ __device__ inline int mla_per_split(int k, int ns) {
 }
 
 struct Partials {
-  float* o;   // [T][ns][H][512]
-  float* ml;  // [T][ns][H][2]  (running max in log2 units, running sum)
+  uint16_t* o;  // [T][ns][H][512] bf16, normalised by the split's own sum
+  float* ml;    // [T][ns][H][2]   (max in log2 units, sum)
 };
 
 __device__ __forceinline__ Partials partials(const MlaArgs& a, int ns) {
   Partials p;
   const size_t T = (size_t)a.row_count;
-  p.o = static_cast<float*>(a.ws);
-  p.ml = p.o + T * ns * a.H * kDV;
+  p.ml = static_cast<float*>(a.ws);
+  p.o = reinterpret_cast<uint16_t*>(p.ml + T * ns * a.H * 2);
   return p;
 }
 
-__global__ __launch_bounds__(kThreads) void k_mla_bf16(MlaArgs a, int ns, int per_split) {
-  __shared__ __attribute__((aligned(16))) unsigned char tile[2][kNT * kRS];
-  __shared__ int vflag[2][kNT];
+// Gather of one tile: wave w moves tile rows 8w..8w+7 (slots j = 0..583 of
+// its region; slot 72 of each row is padding) straight into LDS, 16 bytes per
+// lane per instruction.  Invalid rows read row 0 of the sequence so every
+// instruction is issued with the same lanes (the wait counts stay exact); the
+// row's validity bit masks its score.
+struct TileSrc {
+  const uint16_t* kvb;
+  const int32_t* idx_row;
+  int m1, pos;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void gather_tile(const TileSrc& src, int mb, unsigned char* tile, int* vmask, int wave,
+                                            int lane) {
+  // The indices are wave-uniform: read them with scalar loads so they never
+  // enter the vector-memory counter the tile waits are counted on.
+  int sidx[kRowsPerWave];
+  uint32_t vbits = 0;
+#pragma unroll
+  for (int rr = 0; rr < kRowsPerWave; ++rr) {
+    const int m = __builtin_amdgcn_readfirstlane(mb + wave * kRowsPerWave + rr);
+    const int mc = m < src.m1 ? m : src.m1 - 1;
+    int s = __builtin_amdgcn_readfirstlane(src.idx_row[mc]);
+    s = m < src.m1 ? s : -1;
+    const bool ok = s >= 0 && s <= src.pos;
+    sidx[rr] = ok ? s : 0;
+    vbits |= (ok ? 1u : 0u) << rr;
+  }
+  if (lane == 0) vmask[wave] = (int)vbits;
+  unsigned char* base = tile + wave * kRowsPerWave * kRS;
+#pragma unroll
+  for (int u = 0; u < kDma; ++u) {
+    const int j = 64 * u + lane;
+    const int r0 = (64 * u) / kSlots;  // the instruction's lanes fall in rows r0 and r0 + 1
+    const int rr = j / kSlots;
+    const int piece = j - rr * kSlots;
+    const int s = (rr == r0) ? sidx[r0] : sidx[r0 + 1 < kRowsPerWave ? r0 + 1 : r0];
+    const int pc = piece < kSlots - 1 ? piece : 0;
+    const uint16_t* g = src.kvb + (size_t)s * kDQK + 8 * pc;
+    if (j < kWaveSlots)
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(base + 1024 * u), 16, 0, 0);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32_t* __restrict__ idx, int ns,
+                                                        int per_split, int per_xcd) {
+  __shared__ __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tile1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tile2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char tile3[kTileBytes];
+  __shared__ int vmask[4][kWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int r = (int)blockIdx.x / ns;       // row within this launch
-  const int split = (int)blockIdx.x % ns;
+  // Blocks go round-robin over the 8 XCDs; give each XCD whole queries so the
+  // splits of one query share that XCD's L2 (its query rows are read once).
+  const int li = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+  if (li >= a.row_count * ns) return;
+  const int r = li / ns, split = li % ns;
   const int t = a.row_begin + r;
   const int b = t / a.q_len;
   const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);
   const int m0 = split * per_split;
   const int m1 = min(a.k, m0 + per_split);
   const int ntiles = m1 > m0 ? (m1 - m0 + kNT - 1) / kNT : 0;
-  const bool active = wave * 16 < a.H;
-  const int head = wave * 16 + c;
+  const int h0 = 32 * wave;
+  const bool hb0 = h0 < a.H, hb1 = h0 + 16 < a.H;  // head blocks of this wave
 
-  const int32_t* idx_row = a.idx + (size_t)t * a.k;
-  const uint16_t* kvb = static_cast<const uint16_t*>(a.kv) + (size_t)b * a.S_max * kDQK;
+  TileSrc src;
+  src.kvb = static_cast<const uint16_t*>(a.kv) + (size_t)b * a.S_max * kDQK;
+  src.idx_row = idx + (size_t)t * a.k;
+  src.m1 = m1;
+  src.pos = pos;
 
-  // ---- Q^T fragments: lane holds head (16w + c), dims 32ks + 8g .. +7
-  v8bf qf[kDQK / 32];
-  if (active) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + head) * kDQK + 8 * g;
+  // Q^T fragments: lane holds head h0 + 16*hb + c, dims 32ks + 8g .. +7.
+  v8bf qf[2][kDQK / 32];
 #pragma unroll
-    for (int ks = 0; ks < kDQK / 32; ++ks) qf[ks] = as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks));
+  for (int hb = 0; hb < 2; ++hb) {
+    const bool on = hb ? hb1 : hb0;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + h0 + 16 * hb + c) * kDQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDQK / 32; ++ks)
+      qf[hb][ks] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
   }
 
-  // ---- gather helpers
-  v4i pre[kPPT];
-  auto gather = [&](int tile_i) {
-    const int mb = m0 + tile_i * kNT;
-#pragma unroll
-    for (int j = 0; j < kPPT; ++j) {
-      const int p = tid + j * kThreads;
-      v4i v = {0, 0, 0, 0};
-      if (p < kPieces) {
-        const int row = p / (kRowBytes / 16), q = p % (kRowBytes / 16);
-        const int m = mb + row;
-        const int s = (m < m1) ? idx_row[m] : -1;
-        if (s >= 0 && s <= pos) v = *reinterpret_cast<const v4i*>(kvb + (size_t)s * kDQK + 8 * q);
-      }
-      pre[j] = v;
-    }
-  };
-  auto stage = [&](int tile_i, int buf) {
-    const int mb = m0 + tile_i * kNT;
-#pragma unroll
-    for (int j = 0; j < kPPT; ++j) {
-      const int p = tid + j * kThreads;
-      if (p < kPieces) {
-        const int row = p / (kRowBytes / 16), q = p % (kRowBytes / 16);
-        *reinterpret_cast<v4i*>(&tile[buf][row * kRS + 16 * q]) = pre[j];
-      }
-    }
-    if (tid < kNT) {
-      const int m = mb + tid;
-      const int s = (m < m1) ? idx_row[m] : -1;
-      vflag[buf][tid] = (s >= 0 && s <= pos);
-    }
-  };
+  // Q must be resident before the gather ring starts counting its own loads.
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);  // vmcnt(0)
 
-  // ---- running softmax state (per lane: head c; partial sum over own keys)
-  float m_run = -INFINITY, l_part = 0.f;
-  v4f acc_o[kDV / 16];
-#pragma unroll
-  for (int db = 0; db < kDV / 16; ++db) acc_o[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Zero the ring so rows never written hold finite values.
+  {
+    const v4i z = {0, 0, 0, 0};
+    for (int i = tid; i < kTileBytes / 16; i += kThreads) {
+      reinterpret_cast<v4i*>(tile0)[i] = z;
+      reinterpret_cast<v4i*>(tile1)[i] = z;
+      reinterpret_cast<v4i*>(tile2)[i] = z;
+      reinterpret_cast<v4i*>(tile3)[i] = z;
+    }
+  }
+  // Softmax reference: m_ref is fixed at the first tile with a valid key and
+  // never moved, so the accumulators are never rescaled (they stay in the
+  // MFMA accumulator registers).  Later scores may exceed it by up to 2^64,
+  // which fp32 and bf16 carry exactly as ordinary numbers.  If a score goes
+  // beyond that headroom the block reruns its split once with m_ref set to the
+  // true maximum seen in the first run.
+  float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
+  v4f acc_o[kDV / 16][2];
   const float qk_scale = a.sm_scale * kLog2e;
+  __shared__ int overflow_flag;
+  bool overflow = false;
 
-  if (ntiles > 0) {
-    gather(0);
-    stage(0, 0);
-  }
-  __syncthreads();
-  for (int ti = 0; ti < ntiles; ++ti) {
-    const int buf = ti & 1;
-    if (ti + 1 < ntiles) gather(ti + 1);
-    if (active) {
-      const unsigned char* tb = tile[buf];
-      // S^T blocks: block kb row rho <-> key 8*(rho/4) + 4*kb + rho%4
-      v4f sacc[2];
+  auto compute = [&](const unsigned char* tb, uint32_t valid) {
+    // S^T[key, head]: block kb row rho <-> key 4*(rho/4) + 16*kb + rho%4, so
+    // lane row g holds keys 4g..4g+3 and 16+4g..16+4g+3 of the tile.
+    v4f sacc[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int rho = c;  // A-operand row of this lane
-        const int key = 8 * (rho >> 2) + 4 * kb + (rho & 3);
-        const unsigned char* arow = tb + key * kRS + 16 * g;
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = 4 * (c >> 2) + 16 * kb + (c & 3);
+      const unsigned char* arow = tb + key * kRS + 16 * g;
+      v4f s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < kDQK / 32; ++ks) {
-          const v8bf av = as_v8bf(*reinterpret_cast<const v4i*>(arow + 64 * ks));
-          acc = mfma_bf16(av, qf[ks], acc);
-        }
-        sacc[kb] = acc;
+      for (int ks = 0; ks < kDQK / 32; ++ks) {
+        const v8bf av = as_v8bf(*reinterpret_cast<const v4i*>(arow + 64 * ks));
+        s0 = mfma_bf16(av, qf[0][ks], s0);
+        if (hb1) s1 = mfma_bf16(av, qf[1][ks], s1);
       }
-      // lane (g, c): head c, keys 8g + 4kb + i
+      sacc[kb][0] = s0;
+      sacc[kb][1] = s1;
+    }
+    v8bf pf[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
       float sv[8];
       float tmax = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = 8 * g + 4 * kb + i;
-          const float v = vflag[buf][key] ? sacc[kb][i] * qk_scale : -INFINITY;
+          const int key = 4 * g + 16 * kb + i;
+          const float v = ((valid >> key) & 1u) ? sacc[kb][hb][i] * qk_scale : -INFINITY;
           sv[4 * kb + i] = v;
           tmax = fmaxf(tmax, v);
         }
-      tmax = max_xor16(tmax);
-      tmax = max_xor32(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      float alpha = 1.f;
-      if (m_new != -INFINITY) {
-        alpha = exp2f(m_run - m_new);  // m_run == -inf gives 0
-        float psum = 0.f;
-        uint16_t pb[8];
+      tmax = max_xor32(max_xor16(tmax));
+      m_seen[hb] = fmaxf(m_seen[hb], tmax);
+      if (m_ref[hb] == -INFINITY) m_ref[hb] = tmax;  // nothing accumulated yet
+      if (tmax > m_ref[hb] + 64.f) overflow = true;
+      uint16_t pb[8];
+      float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // the normaliser sums the same bf16-rounded weights the PV product uses,
-          // so the output stays an exact convex combination of the value rows
-          pb[j] = f32_to_bf16_rne(exp2f(sv[j] - m_new));
-          psum += bf16_to_f32(pb[j]);
-        }
-        l_part = l_part * alpha + psum;
-        m_run = m_new;
-        v4i pk;
-        pk[0] = (int)((uint32_t)pb[0] | ((uint32_t)pb[1] << 16));
-        pk[1] = (int)((uint32_t)pb[2] | ((uint32_t)pb[3] << 16));
-        pk[2] = (int)((uint32_t)pb[4] | ((uint32_t)pb[5] << 16));
-        pk[3] = (int)((uint32_t)pb[6] | ((uint32_t)pb[7] << 16));
-        const v8bf pf = as_v8bf(pk);
-        // O^T += V^T . P^T ; V^T fragment via transpose loads:
-        // lane (g, j) supplies key 8g + j/4 (+4), dims 16db + 4*(j%4)
-        const unsigned char* vbase0 = tb + (8 * g + (c >> 2)) * kRS + 2 * 4 * (c & 3);
-        const unsigned char* vbase1 = vbase0 + 4 * kRS;
-#pragma unroll
-        for (int db = 0; db < kDV / 16; ++db) {
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase0 + 32 * db));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vbase1 + 32 * db));
-          const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc_o[db] = mfma_bf16(av, pf, acc_o[db] * alpha);
-        }
+      for (int j = 0; j < 8; ++j) {
+        // the normaliser sums the same bf16-rounded weights the PV product
+        // uses, so the output is an exact convex combination of value rows
+        pb[j] = m_ref[hb] == -INFINITY ? (uint16_t)0 : f32_to_bf16_rne(exp2f(fminf(sv[j] - m_ref[hb], 64.f)));
+        psum += bf16_to_f32(pb[j]);
       }
+      l_part[hb] += psum;
+      v4i pk;
+      pk[0] = (int)((uint32_t)pb[0] | ((uint32_t)pb[1] << 16));
+      pk[1] = (int)((uint32_t)pb[2] | ((uint32_t)pb[3] << 16));
+      pk[2] = (int)((uint32_t)pb[4] | ((uint32_t)pb[5] << 16));
+      pk[3] = (int)((uint32_t)pb[6] | ((uint32_t)pb[7] << 16));
+      pf[hb] = as_v8bf(pk);
     }
-    if (ti + 1 < ntiles) stage(ti + 1, buf ^ 1);
+    // O^T[dims, heads] += V^T[dims, keys] . P^T[keys, heads].  The V^T
+    // fragment (16 dims x keys {4g..4g+3, 16+4g..16+4g+3} for lane row g) is
+    // two LDS transpose loads: lane j of a 16-lane row supplies key
+    // kbase + j/4, dims 16db + 4*(j%4) .. +3.
+    const unsigned char* v0 = tb + (4 * g + (c >> 2)) * kRS + 8 * (c & 3);
+    const unsigned char* v1 = v0 + 16 * kRS;
+#pragma unroll
+    for (int db = 0; db < kDV / 16; ++db) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v0 + 32 * db));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v1 + 32 * db));
+      const v8bf av = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc_o[db][0] = mfma_bf16(av, pf[0], acc_o[db][0]);
+      if (hb1) acc_o[db][1] = mfma_bf16(av, pf[1], acc_o[db][1]);
+    }
+  };
+
+  auto valid_of = [&](int q) -> uint32_t {
+    return (uint32_t)vmask[q][0] | ((uint32_t)vmask[q][1] << 8) | ((uint32_t)vmask[q][2] << 16) |
+           ((uint32_t)vmask[q][3] << 24);
+  };
+  // One ring step: wait for this wave's share of tile t, barrier (all shares
+  // landed; everyone is done with tile t-1), refill the freed buffer with
+  // tile t+3, compute tile t.
+  auto step = [&](int tt, unsigned char* cur, int q, unsigned char* nxt, int qn) {
+    vm_wait(kDma * min(2, ntiles - 1 - tt));
+    ring_barrier();
+    if (tt + 3 < ntiles) gather_tile(src, m0 + (tt + 3) * kNT, nxt, vmask[qn], wave, lane);
+    if (hb0) compute(cur, valid_of(q));
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int db = 0; db < kDV / 16; ++db) acc_o[db][0] = acc_o[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    l_part[0] = l_part[1] = 0.f;
+    if (tid == 0) overflow_flag = 0;
+    __syncthreads();
+    if (ntiles > 0) gather_tile(src, m0, tile0, vmask[0], wave, lane);
+    if (ntiles > 1) gather_tile(src, m0 + kNT, tile1, vmask[1], wave, lane);
+    if (ntiles > 2) gather_tile(src, m0 + 2 * kNT, tile2, vmask[2], wave, lane);
+    for (int tt = 0; tt < ntiles; tt += 4) {
+      step(tt, tile0, 0, tile3, 3);
+      if (tt + 1 < ntiles) step(tt + 1, tile1, 1, tile0, 0);
+      if (tt + 2 < ntiles) step(tt + 2, tile2, 2, tile1, 1);
+      if (tt + 3 < ntiles) step(tt + 3, tile3, 3, tile2, 2);
+    }
+    if (overflow && lane == 0) overflow_flag = 1;
+    __syncthreads();
+    if (!overflow_flag) break;
+    // rerun with the true maxima as references (no score can exceed them)
+    m_ref[0] = m_seen[0];
+    m_ref[1] = m_seen[1];
+    overflow = false;
     __syncthreads();
   }
 
-  if (!active) return;
-  // Reduce the per-lane partial sums over the four lane rows (same head).
-  float l_tot = sum_xor32(sum_xor16(l_part));
-  if (ns == 1) {
+  if (!hb0) return;
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    if (hb == 1 && !hb1) break;
+    const int head = h0 + 16 * hb + c;
+    const float l_tot = sum_xor32(sum_xor16(l_part[hb]));
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + head) * kDV;
+    uint16_t* orow;
+    if (ns == 1) {
+      orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + head) * kDV;
+      if (a.lse && g == 0)
+        a.lse[(size_t)t * a.H + head] = l_tot > 0.f ? (m_ref[hb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    } else {
+      const Partials P = partials(a, ns);
+      orow = P.o + (((size_t)r * ns + split) * a.H + head) * kDV;
+      if (g == 0) {
+        float* pml = P.ml + (((size_t)r * ns + split) * a.H + head) * 2;
+        pml[0] = l_tot > 0.f ? m_ref[hb] : -INFINITY;
+        pml[1] = l_tot;
+      }
+    }
 #pragma unroll
     for (int db = 0; db < kDV / 16; ++db) {
       const int d = 16 * db + 4 * g;
       v2i st;
-      st[0] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(acc_o[db][1] * inv) << 16));
-      st[1] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(acc_o[db][3] * inv) << 16));
+      st[0] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][hb][0] * inv) |
+                    ((uint32_t)f32_to_bf16_rne(acc_o[db][hb][1] * inv) << 16));
+      st[1] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][hb][2] * inv) |
+                    ((uint32_t)f32_to_bf16_rne(acc_o[db][hb][3] * inv) << 16));
       *reinterpret_cast<v2i*>(orow + d) = st;
-    }
-    if (a.lse && g == 0)
-      a.lse[(size_t)t * a.H + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const Partials P = partials(a, ns);
-    float* po = P.o + (((size_t)r * ns + split) * a.H + head) * kDV;
-#pragma unroll
-    for (int db = 0; db < kDV / 16; ++db)
-      *reinterpret_cast<v4f*>(po + 16 * db + 4 * g) = acc_o[db];
-    if (g == 0) {
-      float* pml = P.ml + (((size_t)r * ns + split) * a.H + head) * 2;
-      pml[0] = m_run;
-      pml[1] = l_tot;
     }
   }
 }
 
-// Merge split partials: out = sum_s 2^(m_s-M) O_s / sum_s 2^(m_s-M) l_s.
-template <bool BF16>
+// Merge split partials: each split stored its output normalised by its own
+// sum l_s together with (m_s, l_s); out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s.
 __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, int ns) {
   const int r = (int)blockIdx.x / a.H;
   const int h = (int)blockIdx.x % a.H;
@@ -264,19 +362,20 @@ __global__ __launch_bounds__(128) void k_mla_combine(MlaArgs a, int ns) {
   for (int s = 0; s < ns; ++s) {
     const float* ml = P.ml + (((size_t)r * ns + s) * a.H + h) * 2;
     if (ml[0] == -INFINITY) continue;
-    const float wgt = exp2f(ml[0] - M);
-    wsum += wgt * ml[1];
-    const v4f o = *reinterpret_cast<const v4f*>(P.o + (((size_t)r * ns + s) * a.H + h) * kDV + d);
-    for (int i = 0; i < 4; ++i) acc[i] += wgt * o[i];
+    const float wgt = exp2f(ml[0] - M) * ml[1];
+    wsum += wgt;
+    const v2i o = *reinterpret_cast<const v2i*>(P.o + (((size_t)r * ns + s) * a.H + h) * kDV + d);
+    acc[0] += wgt * bf16_to_f32((uint16_t)(o[0] & 0xFFFF));
+    acc[1] += wgt * bf16_to_f32((uint16_t)((uint32_t)o[0] >> 16));
+    acc[2] += wgt * bf16_to_f32((uint16_t)(o[1] & 0xFFFF));
+    acc[3] += wgt * bf16_to_f32((uint16_t)((uint32_t)o[1] >> 16));
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if (BF16) {
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + h) * kDV + d;
-    v2i st;
-    st[0] = (int)((uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16));
-    st[1] = (int)((uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16));
-    *reinterpret_cast<v2i*>(orow) = st;
-  }
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + h) * kDV + d;
+  v2i st;
+  st[0] = (int)((uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16));
+  st[1] = (int)((uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16));
+  *reinterpret_cast<v2i*>(orow) = st;
   if (a.lse && threadIdx.x == 0)
     a.lse[(size_t)t * a.H + h] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
@@ -344,7 +443,7 @@ size_t mla_workspace_bytes(int T, int H, int k, int is_bf16) {
   if (!is_bf16 || T <= 0) return 0;
   const int ns = mla_splits(T, k);
   if (ns == 1) return 0;
-  return (size_t)T * ns * H * (kDV + 2) * sizeof(float);
+  return (size_t)T * ns * H * (2 * sizeof(float) + kDV * sizeof(uint16_t));
 }
 
 bool mla_f32_supported(int k) { return k <= kF32MaxK; }
@@ -354,9 +453,11 @@ hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
   // Splits are sized from the whole launch so partial buffers match the workspace size query.
   const int ns = mla_splits(a.row_count, a.k);
   const int per = mla_per_split(a.k, ns);
-  hipLaunchKernelGGL(k_mla_bf16, dim3((unsigned)(a.row_count * ns)), dim3(kThreads), 0, stream, a, ns, per);
-  if (ns > 1)
-    hipLaunchKernelGGL(k_mla_combine<true>, dim3((unsigned)(a.row_count * a.H)), dim3(128), 0, stream, a, ns);
+  const int total = a.row_count * ns;
+  const int per_xcd = (total + 7) / 8;
+  hipLaunchKernelGGL(k_mla_bf16, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns, per,
+                     per_xcd);
+  if (ns > 1) hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(a.row_count * a.H)), dim3(128), 0, stream, a, ns);
   return hipGetLastError();
 }
 
