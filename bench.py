@@ -8,9 +8,10 @@ One step = one dsa_forward over one batch of the 128K-context decode workload
 (16 sequences x 2 new queries, context 131072, indexer 64x128 fp8 with
 per-token scales, top-k 2048, 128-head sparse MLA over the bf16 576-wide
 latent cache).  Inputs are seeded synthetic data resident in HBM before the
-timed region.  Before every step a 512 MiB buffer is overwritten so the
-256 MiB last-level cache does not hold the previous step's caches; each step
-is timed with HIP events on the launch stream and ms_per_step is their mean.
+timed region.  Before every step a 512 MiB buffer is read (not written, so no
+dirty lines are left to write back) so the 256 MiB last-level cache does not
+hold the previous step's caches; each step is timed with HIP events on the
+launch stream and ms_per_step is their mean.
 
 Prints ONE JSON line with the headline decode throughput, per-stage timings
 and roofline fractions, the 64K-token prefill throughput, and the float64
@@ -88,7 +89,8 @@ def main():
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = torch.empty(lcl.forward_workspace_size(wl.B, wl.q_len, wl.S_max, H, k, lcl.FP8_E4M3FN, lcl.BF16),
                      dtype=torch.uint8, device=dev)
-    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scrub = torch.ones(128 << 20, dtype=torch.float32, device=dev)  # 512 MiB
+    scrub_out = torch.empty(1, dtype=torch.float32, device=dev)
 
     def forward():
         lcl.forward(geom, k, wl.sm_scale, d["qi"], d["w"], d["ki"], d["qm"], d["kv"], index_k_scale=d["ks"],
@@ -96,7 +98,7 @@ def main():
 
     def evict():
         if not args.no_scrub:
-            scrub.fill_(1)
+            torch.sum(scrub, dim=0, out=scrub_out[0])
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):

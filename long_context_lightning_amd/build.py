@@ -22,6 +22,9 @@ SOURCES = ["api.hip", "indexer.hip", "topk.hip", "prefill.hip", "sparse_mla.hip"
 FLAGS = [
     "-O3",
     "-std=c++17",
+    # no kernel relies on NaN propagation (masks use -inf, which stays
+    # honoured); without this, IEEE mode canonicalises every fmaxf input
+    "-fno-honor-nans",
     "--offload-arch=gfx950",
     "-fPIC",
     "-shared",

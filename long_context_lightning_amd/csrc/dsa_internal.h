@@ -69,6 +69,47 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Head weights of the indexer output rows a lane holds: heads 16m + 4g + i
+// (m, i = 0..3) of query row t, times the optional q-scale.  All loads are
+// issued before any is used (no per-element branches).
+__device__ __forceinline__ void load_head_weights(const void* w, int w_is_bf16, const float* q_scale, size_t t,
+                                                  int g, float (&wv)[4][4]) {
+  if (w_is_bf16) {
+    const uint32_t* w32 = static_cast<const uint32_t*>(w) + (t * 64 + 4 * g) / 2;
+    uint32_t raw[4][2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      raw[m][0] = w32[8 * m];
+      raw[m][1] = w32[8 * m + 1];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      wv[m][0] = __uint_as_float(raw[m][0] << 16);
+      wv[m][1] = __uint_as_float(raw[m][0] & 0xFFFF0000u);
+      wv[m][2] = __uint_as_float(raw[m][1] << 16);
+      wv[m][3] = __uint_as_float(raw[m][1] & 0xFFFF0000u);
+    }
+  } else {
+    const float* wf = static_cast<const float*>(w) + t * 64 + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[m][i] = wf[16 * m + i];
+  }
+  if (q_scale) {
+    const float* qs = q_scale + t * 64 + 4 * g;
+    float sc[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[m][i] = qs[16 * m + i];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[m][i] *= sc[m][i];
+  }
+}
+
 // ------------------------------------------------------------ launch args
 
 struct IndexerArgs {
@@ -83,7 +124,14 @@ struct IndexerArgs {
   int row_begin, row_count;
   float* scores;          // [row_count, ld]
   long long ld;
+  uint32_t* hist;         // optional: per-row histogram of the scores' top 12 order-key bits
+  long long hist_stride;  // words between consecutive rows' histograms
 };
+
+// Histogram bins of the top-k threshold search: the top 12 bits of a score's
+// order key (sign, exponent, 3 mantissa bits).
+constexpr int kHistBins = 4096;
+constexpr int kHistShift = 20;
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerArgs& a, hipStream_t s);
@@ -96,9 +144,12 @@ struct TopkArgs {
   int row_begin, row_count, k;
   int32_t* idx;           // [row_count, k]
   void* ws;
+  int hist_ready;         // 1: the row histograms were already accumulated (by the indexer)
 };
 
 size_t topk_workspace_bytes(int row_count, int S_max, int k);
+long long topk_hist_stride_words(int k);   // per-row stride of the histograms in the workspace
+hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 struct MlaArgs {

@@ -56,8 +56,9 @@ __device__ __forceinline__ RowGroup row_group(const IndexerArgs& a) {
   return RowGroup{b, t0, t1 - t0};
 }
 
-template <int NQ, bool WBF16>
+template <int NQ, bool WBF16, bool HIST>
 __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
+  __shared__ uint32_t lhist[HIST ? NQ * kHistBins : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -82,6 +83,10 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
     for (int r = 0; r < rg.nr; ++r) out[(long long)r * a.ld + s] = -INFINITY;
   if (kend <= chunk0) return;
   const int nsteps = (kend - chunk0 + kKeysPerBlock - 1) / kKeysPerBlock;
+  if (HIST) {
+    for (int i = threadIdx.x; i < NQ * kHistBins; i += 256) lhist[i] = 0u;
+    __syncthreads();
+  }
 
   const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
   const float* ksb = a.k_scale ? a.k_scale + (size_t)rg.b * a.S_max : nullptr;
@@ -109,24 +114,16 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
     const int t = rg.t0 + r;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      if (r < rg.nr) {
-        qf[r][m] = load32(qb + ((size_t)t * kHI + 16 * m + c) * kDI + 32 * g);
+      qf[r][m] = (r < rg.nr) ? load32(qb + ((size_t)t * kHI + 16 * m + c) * kDI + 32 * g)
+                             : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    if (r < rg.nr) {
+      load_head_weights(a.w, WBF16, a.q_scale, (size_t)t, g, wv[r]);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 16 * m + 4 * g + i;
-          float wt;
-          if (WBF16)
-            wt = bf16_to_f32(static_cast<const uint16_t*>(a.w)[(size_t)t * kHI + h]);
-          else
-            wt = static_cast<const float*>(a.w)[(size_t)t * kHI + h];
-          if (a.q_scale) wt *= a.q_scale[(size_t)t * kHI + h];
-          wv[r][m][i] = wt;
-        }
-      } else {
-        qf[r][m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[r][m][i] = 0.f;
-      }
     }
   }
 
@@ -158,12 +155,26 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
       const float a23 = __uint_as_float(p23[0]) + __uint_as_float(p23[1]);
       auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
       const float tot = __uint_as_float(pf[0]) + __uint_as_float(pf[1]);
-      if (r < rg.nr && s_l < kend) out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? tot * ks_cur : -INFINITY;
+      if (r < rg.nr && s_l < kend) {
+        const float v = tot * ks_cur;
+        out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? v : -INFINITY;
+        if (HIST && s_l <= pos[r]) atomicAdd(&lhist[r * kHistBins + (order_key(v) >> kHistShift)], 1u);
+      }
     }
     if (step + 1 < nsteps) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) kf_cur[blk] = kf_nxt[blk];
       ks_cur = ks_nxt;
+    }
+  }
+  if (HIST) {
+    // flush the block's histogram: one global atomic per non-empty bin
+    __syncthreads();
+    for (int i = threadIdx.x; i < NQ * kHistBins; i += 256) {
+      const int r = i / kHistBins;
+      const uint32_t v = lhist[i];
+      if (v && r < rg.nr)
+        atomicAdd(&a.hist[(long long)(rg.t0 + r - a.row_begin) * a.hist_stride + (i - r * kHistBins)], v);
     }
   }
 }
@@ -217,21 +228,28 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
 
 }  // namespace
 
+template <int NQ, bool WBF16>
+static void launch_fp8_variant(const IndexerArgs& a, dim3 grid, hipStream_t stream) {
+  if (a.hist)
+    hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, false>), grid, dim3(256), 0, stream, a);
+}
+
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
   const int b0 = a.row_begin / a.q_len;
   const int b1 = (a.row_begin + a.row_count - 1) / a.q_len;
-  const dim3 block(256);
   const unsigned gx = (unsigned)((a.S_max + kKeysPerChunk - 1) / kKeysPerChunk);
   if (a.q_len == 1) {
     const dim3 grid(gx, (unsigned)(b1 - b0 + 1));
-    if (a.w_is_bf16) hipLaunchKernelGGL((k_indexer_fp8<1, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_indexer_fp8<1, false>), grid, block, 0, stream, a);
+    if (a.w_is_bf16) launch_fp8_variant<1, true>(a, grid, stream);
+    else launch_fp8_variant<1, false>(a, grid, stream);
   } else {
     const int gps = (a.q_len + 1) / 2;
     const dim3 grid(gx, (unsigned)((b1 - b0 + 1) * gps));
-    if (a.w_is_bf16) hipLaunchKernelGGL((k_indexer_fp8<2, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((k_indexer_fp8<2, false>), grid, block, 0, stream, a);
+    if (a.w_is_bf16) launch_fp8_variant<2, true>(a, grid, stream);
+    else launch_fp8_variant<2, false>(a, grid, stream);
   }
   return hipGetLastError();
 }

@@ -229,26 +229,20 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   v8i qf[2][4];
   float wv[2][4][4];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr)
+  for (int rr = 0; rr < 2; ++rr) {
+    const size_t t = (size_t)rt[rr];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (rvalid[rr]) {
-        const size_t t = (size_t)rt[rr];
-        qf[rr][m] = glb_load32(qb8 + (t * kHI + 16 * m + c) * kDI + 32 * g);
+    for (int m = 0; m < 4; ++m)
+      qf[rr][m] = rvalid[rr] ? glb_load32(qb8 + (t * kHI + 16 * m + c) * kDI + 32 * g) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (rvalid[rr]) {
+      load_head_weights(a.w, a.w_is_bf16, a.q_scale, t, g, wv[rr]);
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int h = 16 * m + 4 * g + i;
-          float wt = a.w_is_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.w)[t * kHI + h])
-                                 : static_cast<const float*>(a.w)[t * kHI + h];
-          if (a.q_scale) wt *= a.q_scale[t * kHI + h];
-          wv[rr][m][i] = wt;
-        }
-      } else {
-        qf[rr][m] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wv[rr][m][i] = 0.f;
-      }
     }
+  }
 
   // Key tile staging: thread tid moves 16 bytes (key tid/8, chunk tid%8).
   const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (size_t)b * a.S_max * kDI;

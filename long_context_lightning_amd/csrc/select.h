@@ -13,22 +13,25 @@
 namespace dsa {
 
 // Radix select, largest first, over the values produced by `for_each`
-// (called once per pass with a visitor taking a uint32 value).  Values whose
-// bits above `rem_bits` differ from `prefix` are ignored.  On return `prefix`
-// holds the value v* such that count(v > v*) < want <= count(v >= v*) among
-// the considered values, and `want` is reduced to the number of copies of v*
-// still to take (want - count(v > v*)).  `whist` needs NT/64*256 words, `sm`
-// needs 4 words.  Every thread of the block must call it.
-template <int NT, class ForEach>
+// (called once per pass with a visitor taking a uint32 value), DB bits per
+// pass.  Values whose bits above `rem_bits` differ from `prefix` are ignored.
+// On return `prefix` holds the value v* such that
+// count(v > v*) < want <= count(v >= v*) among the considered values, and
+// `want` is reduced to the number of copies of v* still to take
+// (want - count(v > v*)).  `whist` needs NT/64 << DB words, `sm` 4 words.
+// Every thread of the block must call it.
+template <int NT, int DB, class ForEach>
 __device__ void radix_select_desc(ForEach&& for_each, uint32_t& prefix, int rem_bits, uint32_t& want,
                                   uint32_t* whist, uint32_t* sm) {
   constexpr int NW = NT / 64;
+  constexpr int NB = 1 << DB;
+  constexpr int PER_LANE = NB / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   while (rem_bits > 0) {
-    const int nb = rem_bits < 8 ? rem_bits : 8;
+    const int nb = rem_bits < DB ? rem_bits : DB;
     const int shift = rem_bits - nb;
     const uint32_t dmask = (1u << nb) - 1u;
-    for (int i = tid; i < NW * 256; i += NT) whist[i] = 0u;
+    for (int i = tid; i < NW * NB; i += NT) whist[i] = 0u;
     if (tid == 0) {
       sm[0] = 0u;
       sm[1] = 0u;
@@ -36,37 +39,32 @@ __device__ void radix_select_desc(ForEach&& for_each, uint32_t& prefix, int rem_
     __syncthreads();
     const uint32_t hi = rem_bits >= 32 ? 0u : (prefix >> rem_bits);
     const int rb = rem_bits;
-    uint32_t* mine = whist + wave * 256;
+    uint32_t* mine = whist + wave * NB;
     for_each([&](uint32_t v) {
       if ((rb >= 32 ? 0u : (v >> rb)) == hi) atomicAdd(&mine[(v >> shift) & dmask], 1u);
     });
     __syncthreads();
-    if (tid < 256) {
-      uint32_t s = 0;
-      for (int w = 0; w < NW; ++w) s += whist[w * 256 + tid];
-      whist[tid] = s;  // column sums overwrite wave 0's row (only wave 0's row is read below)
+    for (int i = tid; i < NB; i += NT) {
+      uint32_t c = 0;
+      for (int w = 0; w < NW; ++w) c += whist[w * NB + i];
+      whist[i] = c;  // column sums overwrite wave 0's row (each column read and written by one thread)
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l owns digits 4*(63-l) .. 4*(63-l)+3, i.e. lanes walk digits high -> low
-      const int d0 = 4 * (63 - lane);
-      uint32_t c[4];
+      // lane l owns digits d0 .. d0+PER_LANE-1 with d0 = PER_LANE*(63-l): lanes walk digits high -> low
+      const int d0 = PER_LANE * (63 - lane);
       uint32_t tot = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        c[j] = whist[d0 + 3 - j];  // descending digit order
-        tot += c[j];
-      }
+      for (int j = 0; j < PER_LANE; ++j) tot += whist[d0 + j];
       const uint32_t above = wave_inclusive_sum(tot) - tot;
       if (above < want && want <= above + tot) {
         uint32_t acc = above;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (acc < want && want <= acc + c[j]) {
-            sm[0] = (uint32_t)(d0 + 3 - j);
+        for (int j = PER_LANE - 1; j >= 0; --j) {
+          const uint32_t cj = whist[d0 + j];
+          if (acc < want && want <= acc + cj) {
+            sm[0] = (uint32_t)(d0 + j);
             sm[1] = acc;
           }
-          acc += c[j];
+          acc += cj;
         }
       }
     }

@@ -31,7 +31,10 @@ namespace {
 
 constexpr int kNT = 32;                          // keys per tile
 constexpr int kRowBytes = kDQK * 2;              // 1152
-constexpr int kSlots = kRowBytes / 16 + 1;       // 72 data slots + 1 pad slot per LDS row
+#ifndef DSA_MLA_PAD_SLOTS
+#define DSA_MLA_PAD_SLOTS 1
+#endif
+constexpr int kSlots = kRowBytes / 16 + DSA_MLA_PAD_SLOTS;  // 72 data slots + padding per LDS row
 constexpr int kRS = kSlots * 16;                 // 1168-byte LDS row stride
 constexpr int kTileBytes = kNT * kRS;            // 37376
 constexpr int kWaves = 4;                        // 32 heads per wave -> up to 128 heads
@@ -131,13 +134,16 @@ __device__ __forceinline__ void gather_tile(const TileSrc& src, int mb, unsigned
     const int rr = j / kSlots;
     const int piece = j - rr * kSlots;
     const int s = (rr == r0) ? sidx[r0] : sidx[r0 + 1 < kRowsPerWave ? r0 + 1 : r0];
-    const int pc = piece < kSlots - 1 ? piece : 0;
+    const int pc = piece < kRowBytes / 16 ? piece : 0;
     const uint16_t* g = src.kvb + (size_t)s * kDQK + 8 * pc;
     if (j < kWaveSlots)
       __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(base + 1024 * u), 16, 0, 0);
   }
 }
 
+// FULL: every wave owns two 16-head blocks (H a multiple of 32), so the
+// second block needs no runtime guard.
+template <bool FULL>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32_t* __restrict__ idx, int ns,
                                                         int per_split, int per_xcd) {
   __shared__ __attribute__((aligned(16))) unsigned char tile0[kTileBytes];
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   const int m1 = min(a.k, m0 + per_split);
   const int ntiles = m1 > m0 ? (m1 - m0 + kNT - 1) / kNT : 0;
   const int h0 = 32 * wave;
-  const bool hb0 = h0 < a.H, hb1 = h0 + 16 < a.H;  // head blocks of this wave
+  const bool hb0 = h0 < a.H, hb1 = FULL || (h0 + 16 < a.H);  // head blocks of this wave
 
   TileSrc src;
   src.kvb = static_cast<const uint16_t*>(a.kv) + (size_t)b * a.S_max * kDQK;
@@ -228,35 +234,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
     for (int hb = 0; hb < 2; ++hb) {
       float sv[8];
       float tmax = -INFINITY;
+      if (valid == 0xFFFFFFFFu) {  // full tile: no masking
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = 4 * g + 16 * kb + i;
-          const float v = ((valid >> key) & 1u) ? sacc[kb][hb][i] * qk_scale : -INFINITY;
-          sv[4 * kb + i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+          for (int i = 0; i < 4; ++i) {
+            sv[4 * kb + i] = sacc[kb][hb][i] * qk_scale;
+            tmax = fmaxf(tmax, sv[4 * kb + i]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 4 * g + 16 * kb + i;
+            const float v = ((valid >> key) & 1u) ? sacc[kb][hb][i] * qk_scale : -INFINITY;
+            sv[4 * kb + i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
       tmax = max_xor32(max_xor16(tmax));
       m_seen[hb] = fmaxf(m_seen[hb], tmax);
       if (m_ref[hb] == -INFINITY) m_ref[hb] = tmax;  // nothing accumulated yet
       if (tmax > m_ref[hb] + 64.f) overflow = true;
-      uint16_t pb[8];
+      // p = 2^(s - m_ref) rounded to bf16 (v_exp_f32 + v_cvt_pk_bf16_f32, RNE);
+      // the normaliser sums the same rounded weights the PV product uses, so
+      // the output is an exact convex combination of value rows.
+      const float mr = m_ref[hb] == -INFINITY ? INFINITY : m_ref[hb];  // no reference yet: all p = 0
+      v8bf pv;
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        // the normaliser sums the same bf16-rounded weights the PV product
-        // uses, so the output is an exact convex combination of value rows
-        pb[j] = m_ref[hb] == -INFINITY ? (uint16_t)0 : f32_to_bf16_rne(exp2f(fminf(sv[j] - m_ref[hb], 64.f)));
-        psum += bf16_to_f32(pb[j]);
+        pv[j] = (__bf16)__builtin_amdgcn_exp2f(fminf(sv[j] - mr, 64.f));
+        psum += (float)pv[j];
       }
       l_part[hb] += psum;
-      v4i pk;
-      pk[0] = (int)((uint32_t)pb[0] | ((uint32_t)pb[1] << 16));
-      pk[1] = (int)((uint32_t)pb[2] | ((uint32_t)pb[3] << 16));
-      pk[2] = (int)((uint32_t)pb[4] | ((uint32_t)pb[5] << 16));
-      pk[3] = (int)((uint32_t)pb[6] | ((uint32_t)pb[7] << 16));
-      pf[hb] = as_v8bf(pk);
+      pf[hb] = pv;
     }
     // O^T[dims, heads] += V^T[dims, keys] . P^T[keys, heads].  The V^T
     // fragment (16 dims x keys {4g..4g+3, 16+4g..16+4g+3} for lane row g) is
@@ -455,8 +468,12 @@ hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
   const int per = mla_per_split(a.k, ns);
   const int total = a.row_count * ns;
   const int per_xcd = (total + 7) / 8;
-  hipLaunchKernelGGL(k_mla_bf16, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns, per,
-                     per_xcd);
+  if (a.H % 32 == 0)
+    hipLaunchKernelGGL(k_mla_bf16<true>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns,
+                       per, per_xcd);
+  else
+    hipLaunchKernelGGL(k_mla_bf16<false>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns,
+                       per, per_xcd);
   if (ns > 1) hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(a.row_count * a.H)), dim3(128), 0, stream, a, ns);
   return hipGetLastError();
 }

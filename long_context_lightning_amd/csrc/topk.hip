@@ -8,10 +8,12 @@
 //  1. zero   -- clear the per-row histograms and counters in the workspace.
 //  2. hist   -- (row, 8192-score segment) blocks: LDS histogram of the top 12
 //               bits of each score's order key, flushed with global atomics.
+//               (dsa_forward skips 1-2 here: it zeroes before the indexer,
+//               whose epilogue accumulates the same histogram.)
 //  3. gather -- same blocks: every block finds the threshold bin b* (the bin
 //               holding the k-th largest) from the row histogram and appends
 //               the (key, position) of every score in bins >= b* to the row's
-//               candidate list (wave-aggregated atomics).
+//               candidate list, reserving its range with one atomic.
 //  4. final  -- one 1024-thread block per row: exact radix select of the k-th
 //               key inside bin b*, lower-position tie-break by a second
 //               radix select on positions, then the chosen positions are
@@ -25,11 +27,12 @@ namespace dsa {
 
 namespace {
 
-constexpr int kBins = 4096;     // top 12 bits of the order key
-constexpr int kBinShift = 20;
+constexpr int kBins = kHistBins;       // top 12 bits of the order key
+constexpr int kBinShift = kHistShift;
 constexpr int kSeg = 8192;      // scores per hist/gather block
 constexpr int kSegThreads = 256;
-constexpr int kFinThreads = 1024;
+constexpr int kFinThreads = 256;
+constexpr int kDigitBits = 11;  // radix digit width of the exact selection
 constexpr int kMaxK = 4096;
 constexpr int kMaxS = 262144;
 
@@ -127,7 +130,9 @@ __device__ void find_threshold_bin(const uint32_t* hist, uint32_t k, uint32_t* s
 }
 
 __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
+  constexpr int kPer = kSeg / kSegThreads;  // scores per thread
   __shared__ uint32_t sm[kSegThreads / 64 + 4];
+  __shared__ uint32_t base_sh;
   const int r = blockIdx.y;
   const int n = row_valid_count(a, r);
   const int seg0 = (int)blockIdx.x * kSeg;
@@ -138,24 +143,28 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
   if ((size_t)above + w.hist[bstar] > cap_for(a.k)) return;  // final block takes the direct path
   const float* row = a.scores + (long long)r * a.ld;
   const int e1 = min(seg0 + kSeg, n);
-  const int lane = threadIdx.x & 63;
-  for (int e0 = seg0; e0 < e1; e0 += kSegThreads) {
-    const int e = e0 + (int)threadIdx.x;
-    uint32_t key = 0;
-    bool pred = false;
-    if (e < e1) {
-      key = order_key(row[e]);
-      pred = (key >> kBinShift) >= bstar;
-    }
-    const unsigned long long ball = __ballot(pred);
-    if (ball == 0ull) continue;
-    uint32_t base = 0;
-    if (lane == 0) base = atomicAdd(&w.meta[0], (uint32_t)__popcll(ball));
-    base = __shfl(base, 0, 64);
-    if (pred) {
-      const uint32_t slot = base + (uint32_t)__popcll(ball & ((1ull << lane) - 1ull));
-      w.ekey[slot] = key;
-      w.eidx[slot] = (uint32_t)e;
+  // Keys of this thread's scores stay in registers; one reservation per block.
+  uint32_t key[kPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = seg0 + (int)threadIdx.x + j * kSegThreads;
+    key[j] = e < e1 ? order_key(row[e]) : 0u;
+    mine += (e < e1 && (key[j] >> kBinShift) >= bstar) ? 1u : 0u;
+  }
+  uint32_t total;
+  uint32_t off = block_exclusive_sum<kSegThreads>(mine, sm, &total);
+  if (total == 0) return;
+  if (threadIdx.x == 0) base_sh = atomicAdd(&w.meta[0], total);
+  __syncthreads();
+  off += base_sh;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = seg0 + (int)threadIdx.x + j * kSegThreads;
+    if (e < e1 && (key[j] >> kBinShift) >= bstar) {
+      w.ekey[off] = key[j];
+      w.eidx[off] = (uint32_t)e;
+      ++off;
     }
   }
 }
@@ -163,8 +172,8 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
 __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   extern __shared__ uint32_t dyn[];
   constexpr int NW = kFinThreads / 64;
-  uint32_t* whist = dyn;                 // NW * 256
-  uint32_t* sm = whist + NW * 256;       // 64
+  uint32_t* whist = dyn;                          // NW << kDigitBits
+  uint32_t* sm = whist + (NW << kDigitBits);      // 64
   uint32_t* bitmap = sm + 64;            // ceil(S_max/32)
   const int Wmax = (a.S_max + 31) >> 5;
   uint32_t* skey = bitmap + Wmax;        // cap
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
     // Entries with bin > b* are all taken; resolve the rest inside bin b*.
     tau = bstar << kBinShift;
     want = (uint32_t)a.k - above;
-    radix_select_desc<kFinThreads>(
+    radix_select_desc<kFinThreads, kDigitBits>(
         [&](auto f) {
           for (uint32_t i = tid; i < total; i += kFinThreads) f(skey[i]);
         },
@@ -203,7 +212,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   } else {
     tau = 0u;
     want = (uint32_t)a.k;
-    radix_select_desc<kFinThreads>(
+    radix_select_desc<kFinThreads, kDigitBits>(
         [&](auto f) {
           for (int e = tid; e < n; e += kFinThreads) f(order_key(row[e]));
         },
@@ -227,24 +236,26 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   __syncthreads();
   uint32_t cut = 0xFFFFFFFFu;  // positions <= cut among the ties are taken
   if (want < eq_total) {
+    // the want lowest positions = the want largest of (top - position), top < 2^18
+    const uint32_t top = (uint32_t)kMaxS - 1u;
     uint32_t inv = 0u;
     uint32_t wv = want;
     if (!direct) {
-      radix_select_desc<kFinThreads>(
+      radix_select_desc<kFinThreads, kDigitBits>(
           [&](auto f) {
             for (uint32_t i = tid; i < total; i += kFinThreads)
-              if (skey[i] == tau) f(~sidx[i]);
+              if (skey[i] == tau) f(top - sidx[i]);
           },
-          inv, 32, wv, whist, sm);
+          inv, 18, wv, whist, sm);
     } else {
-      radix_select_desc<kFinThreads>(
+      radix_select_desc<kFinThreads, kDigitBits>(
           [&](auto f) {
             for (int e = tid; e < n; e += kFinThreads)
-              if (order_key(row[e]) == tau) f(~(uint32_t)e);
+              if (order_key(row[e]) == tau) f(top - (uint32_t)e);
           },
-          inv, 32, wv, whist, sm);
+          inv, 18, wv, whist, sm);
     }
-    cut = ~inv;
+    cut = top - inv;
   }
   const int W = (n + 31) >> 5;
   for (int i = tid; i < W; i += kFinThreads) bitmap[i] = 0u;
@@ -266,10 +277,18 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
 }
 
 size_t final_lds_bytes(int S_max, int k) {
-  return ((size_t)(kFinThreads / 64) * 256 + 64 + ((S_max + 31) >> 5) + 2 * cap_for(k)) * 4;
+  return (((size_t)(kFinThreads / 64) << kDigitBits) + 64 + ((S_max + 31) >> 5) + 2 * cap_for(k)) * 4;
 }
 
 }  // namespace
+
+long long topk_hist_stride_words(int k) { return (long long)(row_stride_bytes(k) / 4); }
+
+hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t stream) {
+  if (a.row_count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 size_t topk_workspace_bytes(int row_count, int S_max, int k) {
   (void)S_max;
@@ -283,9 +302,11 @@ bool topk_supported(int S_max, int k) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
   const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);
-  hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
+  if (!a.hist_ready) {
+    hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
+  }
   hipLaunchKernelGGL(k_topk_gather, segs, dim3(kSegThreads), 0, stream, a);
   const size_t lds = final_lds_bytes(a.S_max, a.k);
   hipLaunchKernelGGL(k_topk_final, dim3((unsigned)a.row_count), dim3(kFinThreads), lds, stream, a);
