@@ -43,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scrub", action="store_true", help="do not evict the last-level cache between steps")
     ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="run the CPU oracle on whole decode sequences until this much time has passed")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 256 MiB device copy (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -56,15 +60,23 @@ def main():
     import torch
 
     import long_context_lightning_amd as lcl
-    from synth import baseline_workload
+    from synth import standard_workload
 
     lcl.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    if args.copy_probe:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 268435456 bytes read, 268435456 bytes written")
+        del src, dst
+
     # ------------------------------------------------------------ decode 128K
-    wl = baseline_workload("decode128k")
+    wl = standard_workload("decode128k")
     log(f"generating {wl.name}: B={wl.B} q_len={wl.q_len} S={wl.S_max} k={wl.topk} H={wl.H}")
     t0 = time.time()
     qi, w = wl.qi(), wl.w()
@@ -154,10 +166,29 @@ def main():
         stages[n] = {"us": round(st_ms[n] * 1e3, 2), "bytes": stage_bytes[n], "GB_s": round(gbs, 1),
                      "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"  {n:10s} {st_ms[n] * 1e3:8.1f} us  {gbs:8.1f} GB/s  ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
-    dom = max(st_ms, key=st_ms.get)
-    dom_gbs = stage_bytes[dom] / (st_ms[dom] * 1e-3) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    # The longest kernel of a decode step is the indexer's (one launch of
+    # k_indexer_fp8 per dsa_indexer_scores call here; the step's copy also
+    # accumulates the top-k histogram).  Its launch duration is timed over
+    # back-to-back launches (the 276.8 MB K read exceeds the 256 MiB
+    # last-level cache, so each launch streams it from HBM again), which
+    # keeps the per-launch dispatch latency of an event pair out of it.  Its
+    # measured HBM traffic per launch comes from the committed counter
+    # summary, valid only for the sources it was taken on.
+    reps = 10
+    evict()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    for _ in range(reps):
+        lcl.indexer_scores(geom, d["qi"], d["w"], d["ki"], k_scale=d["ks"], scores=scores)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    dom_us = e[0].elapsed_time(e[1]) * 1e3 / reps
+    dom_gbs = stage_bytes["indexer"] / (dom_us * 1e-6) / 1e9
+    log(f"  k_indexer_fp8 back-to-back: {dom_us:.1f} us/launch = {dom_gbs:.1f} GB/s")
+    roofline = {"kernel": "k_indexer_fp8 (decode128k, 32 rows x 131072 keys)", "bound": "hbm",
+                "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "us_per_launch": round(dom_us, 2),
+                "traffic": measured_traffic("indexer_fp8_decode128k")}
     del scores
 
     # --------------------------------------------------------- prefill 64K
@@ -170,7 +201,7 @@ def main():
     # ------------------------------------------------------ CPU baseline
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, qi, w, ki, ks, qm, np)
+        cpu = cpu_baseline(wl, qi, w, ki, ks, qm, np, args.cpu_seconds)
 
     line = {
         "metric": "DSA decode queries/s @128K ctx (dsa_forward: indexer + top-k + sparse MLA)",
@@ -195,6 +226,32 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(name):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain copy) from profiles/<name>_traffic.txt, or None when that file is
+    missing or was taken on different kernel sources."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "#", "|")):
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    h = hashlib.sha256()
+    for src in fields.get("sources", "").split():
+        with open(os.path.join(here, src), "rb") as f:
+            h.update(f.read())
+    if not fields.get("sources") or h.hexdigest() != fields.get("sources_sha256"):
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def bench_prefill(args, lcl, torch, np, dev, stream, evict):
@@ -260,24 +317,28 @@ def bench_prefill(args, lcl, torch, np, dev, stream, evict):
     return res
 
 
-def cpu_baseline(wl, qi, w, ki, ks, qm, np):
-    """The float64 oracle on a bounded sample: the queries of the first
-    sequences of the decode workload, through all three stages."""
+def cpu_baseline(wl, qi, w, ki, ks, qm, np, budget_s):
+    """The float64 oracle on a bounded sample of the decode workload: whole
+    sequences (both queries, all three stages), one after another, until
+    budget_s seconds of oracle time have passed (at least one sequence)."""
     import oracle
     cores = len(os.sched_getaffinity(0))
-    nseq = 2
-    rows = np.arange(nseq * wl.q_len)
-    log(f"cpu baseline: oracle on {len(rows)} decode queries ({nseq} sequences), {cores} cores")
-    kv = np.stack([wl.kv(b) for b in range(nseq)] + [np.zeros((1, 576), np.uint16)] * 0)
-    t0 = time.perf_counter()
-    seq = wl.seq_lens[:nseq]
-    oracle.dsa_forward(qi[rows], "e4m3fn", w[rows], "bf16", ki[:nseq], "e4m3fn", qm[rows], "bf16", kv, "bf16",
-                       seq, wl.q_len, wl.topk, wl.sm_scale, k_scale=ks[:nseq])
-    dt = time.perf_counter() - t0
-    log(f"cpu baseline: {dt:.1f}s for {len(rows)} queries")
-    return {"value": round(len(rows) / dt, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(rows)} queries ({nseq} sequences x {wl.q_len}) of the 128K decode workload, "
-                      f"all three stages in float64 NumPy"}
+    log(f"cpu baseline: oracle on whole decode sequences for ~{budget_s:.0f}s, {cores} cores")
+    spent, nseq = 0.0, 0
+    while nseq < wl.B and (nseq == 0 or spent < budget_s):
+        b = nseq
+        rows = np.arange(b * wl.q_len, (b + 1) * wl.q_len)
+        kv = wl.kv(b)[None]
+        t0 = time.perf_counter()
+        oracle.dsa_forward(qi[rows], "e4m3fn", w[rows], "bf16", ki[b:b + 1], "e4m3fn", qm[rows], "bf16", kv,
+                           "bf16", wl.seq_lens[b:b + 1], wl.q_len, wl.topk, wl.sm_scale, k_scale=ks[b:b + 1])
+        spent += time.perf_counter() - t0
+        nseq += 1
+    nq = nseq * wl.q_len
+    log(f"cpu baseline: {spent:.1f}s for {nq} queries")
+    return {"value": round(nq / spent, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nq} queries ({nseq} of the {wl.B} sequences x {wl.q_len}) of the 128K decode workload, "
+                      f"all three stages in float64 NumPy, {spent:.1f}s"}
 
 
 if __name__ == "__main__":

@@ -126,7 +126,9 @@ DSA_API dsa_status dsa_indexer_scores(const dsa_geom* geom,
  * be NaN (NaN rows give an unspecified but in-range selection).
  *
  *   scores [row_count, ld] fp32, ld >= S_max;  idx [row_count, k] int32
- *   1 <= k <= 16384;  ws >= dsa_topk_workspace_size(...) bytes. */
+ *   k >= 1 (else DSA_ERR_INVALID_ARG); this build selects for k <= 4096
+ *   and S_max <= 262144 and returns DSA_ERR_UNSUPPORTED beyond;
+ *   ws >= dsa_topk_workspace_size(...) bytes. */
 DSA_API dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld,
                     int32_t row_begin, int32_t row_count, int32_t k,
                     int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);

@@ -14,7 +14,7 @@
 //               holding the k-th largest) from the row histogram and appends
 //               the (key, position) of every score in bins >= b* to the row's
 //               candidate list, reserving its range with one atomic.
-//  4. final  -- one 1024-thread block per row: exact radix select of the k-th
+//  4. final  -- one 256-thread block per row: exact radix select of the k-th
 //               key inside bin b*, lower-position tie-break by a second
 //               radix select on positions, then the chosen positions are
 //               marked in an LDS bitmap and written out in ascending order.

@@ -20,7 +20,6 @@ the passage of the pages it follows:
 * "NSA 与 DSA" (luowle page) section 3.2: public config 64 heads x 128 dims,
   top-k 2048, one shared indexer key per token.
 
-Readings of points the pages leave open are listed in the design doc.
 """
 
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_times_512

@@ -7,7 +7,7 @@ workloads); none of the indexer, top-k or attention arithmetic lives here.
 """
 
 from .encode import encode_bf16_rne, encode_e4m3fn_rne, quantize_per_token
-from .workloads import Workload, make_workload, baseline_workload, BASELINE_NAMES
+from .workloads import Workload, make_workload, standard_workload, WORKLOAD_NAMES
 
 __all__ = [
     "encode_bf16_rne",
@@ -15,6 +15,6 @@ __all__ = [
     "quantize_per_token",
     "Workload",
     "make_workload",
-    "baseline_workload",
-    "BASELINE_NAMES",
+    "standard_workload",
+    "WORKLOAD_NAMES",
 ]

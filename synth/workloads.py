@@ -263,10 +263,10 @@ def make_workload(name, B, q_len, seq_lens, S_max, topk, H, fp8=True, seed=0,
                     plant=plant)
 
 
-BASELINE_NAMES = ("tiny512", "decode32k", "prefill8k", "prefill64k", "decode128k")
+WORKLOAD_NAMES = ("tiny512", "decode32k", "prefill8k", "prefill64k", "decode128k")
 
 
-def baseline_workload(name):
+def standard_workload(name):
     """The five configurations at their full sizes."""
     if name == "tiny512":
         return make_workload(name, 1, 512, 512, 512, 64, 16, fp8=False, seed=0)

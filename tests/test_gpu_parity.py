@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import query_positions, topk_select
-from synth import baseline_workload, make_workload
+from synth import standard_workload, make_workload
 from tests.gpu_util import Uploaded, check_attention, check_scores, check_topk, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -142,7 +142,7 @@ def test_forward(dsa_gpu, case):
 
 def test_full_tiny512(dsa_gpu):
     _say("[full] tiny512 (fp32 throughout)")
-    wl = baseline_workload("tiny512")
+    wl = standard_workload("tiny512")
     up = Uploaded(wl)
     g = up.geom(dsa_gpu)
     sc = dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki)
@@ -160,7 +160,7 @@ def test_full_tiny512(dsa_gpu):
 @pytest.mark.parametrize("name", ["decode32k", "decode128k"])
 def test_full_decode(dsa_gpu, name):
     _say(f"[full] {name}")
-    wl = baseline_workload(name)
+    wl = standard_workload(name)
     up = Uploaded(wl)
     g = up.geom(dsa_gpu)
     idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
@@ -181,7 +181,7 @@ def test_full_decode(dsa_gpu, name):
 
 def test_full_prefill8k_planted(dsa_gpu):
     _say("[full] prefill8k planted (streaming path)")
-    wl = baseline_workload("prefill8k")
+    wl = standard_workload("prefill8k")
     rng = np.random.default_rng(1)
     sample = np.unique(np.concatenate([wl.planted_rows, [0, 1, 2046, 2047, 2048, 2049, 8191],
                                        rng.choice(8192, 24, replace=False)]))
@@ -200,7 +200,7 @@ def test_full_prefill8k_planted(dsa_gpu):
 
 def test_full_prefill64k_sampled(dsa_gpu):
     _say("[full] prefill64k sampled rows (streaming path)")
-    wl = baseline_workload("prefill64k")
+    wl = standard_workload("prefill64k")
     rng = np.random.default_rng(2)
     k = wl.topk
     sample = np.unique(np.concatenate([[0, 1, 2, k - 2, k - 1, k, k + 1], np.arange(65536 - 8, 65536),

@@ -17,7 +17,7 @@ import pytest
 from scipy.special import logsumexp, softmax
 
 from oracle import dsa_forward, sparse_mla, query_positions
-from synth import baseline_workload, make_workload
+from synth import standard_workload, make_workload
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_case.json")
 
@@ -78,7 +78,7 @@ def test_dsa_equals_dense_causal_when_nothing_is_dropped():
 
 def test_tiny_config_first_rows_are_dense():
     """The tiny 512-token configuration: rows t < 64 keep everything (k = 64)."""
-    w = baseline_workload("tiny512")
+    w = standard_workload("tiny512")
     rows = np.array([0, 1, 31, 63, 64, 300])
     qi, ww, (ki, ks), qm, kv = w.qi(), w.w(), w.ki_all(), w.qm(), w.kv_all()
     idx, tau, out, lse, _ = dsa_forward(qi, "f32", ww, "f32", ki, "f32", qm, "f32", kv,

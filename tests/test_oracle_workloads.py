@@ -11,11 +11,11 @@ Also: the lazily drawn inputs are reproducible row by row.
 import numpy as np
 
 from oracle import indexer_scores, topk_select
-from synth import baseline_workload, make_workload
+from synth import standard_workload, make_workload
 
 
 def test_planted_rows_select_the_planted_set():
-    w = baseline_workload("prefill8k")
+    w = standard_workload("prefill8k")
     rows = w.planted_rows
     assert len(rows) == 32 and rows.min() >= 4096
     k, ks = w.ki(0)
@@ -34,12 +34,12 @@ def test_planted_rows_select_the_planted_set():
 
 
 def test_rows_regenerate_bit_exactly():
-    w = baseline_workload("prefill8k")
+    w = standard_workload("prefill8k")
     rows = np.array([5, 4097, 8191, 64, 63])
     full_q = w.qi(np.arange(0, 130))
     assert np.array_equal(w.qi(rows[[0, 3, 4]]), full_q[[5, 64, 63]])
     assert np.array_equal(w.w(rows), w.w(rows))
-    w2 = baseline_workload("prefill8k")
+    w2 = standard_workload("prefill8k")
     assert np.array_equal(w2.qm(rows), w.qm(rows))
     assert np.array_equal(w2.kv(0)[:100], w.kv(0)[:100])
 
@@ -64,8 +64,8 @@ def test_pool_keys_produce_exact_ties_resolved_to_lower_index():
         assert idx.tolist() == _brute(row, pos[t], w.topk)
 
 
-def test_baseline_shapes():
-    shapes = {n: baseline_workload(n) for n in
+def test_standard_shapes():
+    shapes = {n: standard_workload(n) for n in
               ("tiny512", "decode32k", "prefill8k", "prefill64k", "decode128k")}
     assert shapes["tiny512"].T == 512 and shapes["tiny512"].topk == 64 and shapes["tiny512"].H == 16
     assert shapes["decode32k"].T == 64 and shapes["decode32k"].S_max == 32768
