@@ -6,14 +6,25 @@
 
 namespace dsa {
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Value of lane (l - n) within the same 16-lane row for lanes of the rows
+// in ROW_MASK (0 where that lane is outside the row), else 0; DPP CTRL.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_take(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP: a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8), then
+// row_bcast:15 carries each even row's total into the next row and
+// row_bcast:31 carries lanes 0..31's total into lanes 32..63.  Every lane of
+// the wave must be active.
 __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v += dpp_take<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_take<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_take<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_take<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_take<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_take<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

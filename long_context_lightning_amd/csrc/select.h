@@ -76,25 +76,79 @@ __device__ void radix_select_desc(ForEach&& for_each, uint32_t& prefix, int rem_
   }
 }
 
-// Write the set bits of `bitmap` (n bits, positions 0..n-1) as ascending
-// positions to out[0..].  Returns the number written.  Block-wide.
+// Bitmap tail of a selection.  `bitmap` holds the positions with key > tau,
+// `tbits` the copies of tau; both cover n positions in W = ceil(n/32) words
+// and are zero up to the next multiple of 4 words (they are read 16 bytes at
+// a time).  Keeps the `want` lowest-position copies of tau (want >= 1),
+// folds them into `bitmap`, and writes all set positions in ascending order
+// to out[0..limit).  Thread t owns the contiguous words
+// [t*per, (t+1)*per), per a multiple of 4.  Returns the number of set
+// positions.  `sm` needs NT/64 + 4 words.  Block-wide.
 template <int NT>
-__device__ uint32_t bitmap_to_sorted(const uint32_t* bitmap, int n, int32_t* out, uint32_t limit, uint32_t* sm) {
-  const int W = (n + 31) >> 5;
-  const int per = (W + NT - 1) / NT;
-  const int w0 = (int)threadIdx.x * per;
-  const int w1 = min(w0 + per, W);
+__device__ uint32_t bitmap_select_emit(uint32_t* bitmap, const uint32_t* tbits, int n, uint32_t want, int32_t* out,
+                                       uint32_t limit, uint32_t* sm) {
+  constexpr int NW = NT / 64;
+  const int W4 = (((n + 31) >> 5) + 3) >> 2;  // 16-byte groups
+  const int per4 = (W4 + NT - 1) / NT;
+  const int g0 = (int)threadIdx.x * per4, g1 = min(g0 + per4, W4);
+  const v4i* t4 = reinterpret_cast<const v4i*>(tbits);
+  v4i* b4 = reinterpret_cast<v4i*>(bitmap);
+  // 1. the want-th set bit of tbits (in position order) is the last copy kept
+  uint32_t c = 0;
+  for (int gi = g0; gi < g1; ++gi) {
+    const v4i t = t4[gi];
+    c += __popc((uint32_t)t[0]) + __popc((uint32_t)t[1]) + __popc((uint32_t)t[2]) + __popc((uint32_t)t[3]);
+  }
+  if (threadIdx.x == 0) sm[NW + 2] = 0xFFFFFFFFu;
+  uint32_t tot;
+  uint32_t acc = block_exclusive_sum<NT>(c, sm, &tot);
+  if (acc < want && want <= acc + c) {
+    for (int gi = g0; gi < g1; ++gi) {
+      const v4i t = t4[gi];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t bits = (uint32_t)t[j];
+        const uint32_t pc = __popc(bits);
+        if (acc < want && want <= acc + pc) {
+          for (uint32_t r = want - acc; r > 1; --r) bits &= bits - 1u;
+          sm[NW + 2] = 32u * (uint32_t)(4 * gi + j) + (uint32_t)(__ffs(bits) - 1);
+        }
+        acc += pc;
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t cut = sm[NW + 2];
+  const int cw = (int)(cut >> 5);
+  const uint32_t cmask = (2u << (cut & 31)) - 1u;  // bits <= cut within word cw
+  // 2. fold the kept copies into bitmap and count
   uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+  for (int gi = g0; gi < g1; ++gi) {
+    const v4i t = t4[gi];
+    v4i b = b4[gi];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int wi = 4 * gi + j;
+      const uint32_t keep = wi < cw ? 0xFFFFFFFFu : (wi == cw ? cmask : 0u);
+      b[j] = (int)((uint32_t)b[j] | ((uint32_t)t[j] & keep));
+      cnt += __popc((uint32_t)b[j]);
+    }
+    b4[gi] = b;
+  }
   uint32_t total;
   uint32_t off = block_exclusive_sum<NT>(cnt, sm, &total);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t bits = bitmap[w];
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      if (off < limit) out[off] = 32 * w + b;
-      ++off;
-      bits &= bits - 1u;
+  // 3. positions in ascending order
+  for (int gi = g0; gi < g1; ++gi) {
+    const v4i b = b4[gi];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t bits = (uint32_t)b[j];
+      while (bits) {
+        const int bb = __ffs(bits) - 1;
+        if (off < limit) out[off] = 32 * (4 * gi + j) + bb;
+        ++off;
+        bits &= bits - 1u;
+      }
     }
   }
   return total;

@@ -14,10 +14,11 @@
 //               holding the k-th largest) from the row histogram and appends
 //               the (key, position) of every score in bins >= b* to the row's
 //               candidate list, reserving its range with one atomic.
-//  4. final  -- one 256-thread block per row: exact radix select of the k-th
-//               key inside bin b*, lower-position tie-break by a second
-//               radix select on positions, then the chosen positions are
-//               marked in an LDS bitmap and written out in ascending order.
+//  4. final  -- one 256-thread block per row: exact radix select (8-bit
+//               digits) of the k-th key tau inside bin b*; positions with
+//               key > tau and the copies of tau go into two LDS bitmaps; the
+//               lower-position tie rule keeps the copies up to the want-th
+//               set bit of the second; both are written out in ascending order.
 //               If the candidate list would overflow (scores concentrated
 //               in one bin) the block selects directly from the score row.
 #include "dsa_internal.h"
@@ -32,7 +33,7 @@ constexpr int kBinShift = kHistShift;
 constexpr int kSeg = 8192;      // scores per hist/gather block
 constexpr int kSegThreads = 256;
 constexpr int kFinThreads = 256;
-constexpr int kDigitBits = 11;  // radix digit width of the exact selection
+constexpr int kDigitBits = 8;   // radix digit width of the exact selection
 constexpr int kMaxK = 4096;
 constexpr int kMaxS = 262144;
 
@@ -170,13 +171,14 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
 }
 
 __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
-  extern __shared__ uint32_t dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   constexpr int NW = kFinThreads / 64;
   uint32_t* whist = dyn;                          // NW << kDigitBits
   uint32_t* sm = whist + (NW << kDigitBits);      // 64
-  uint32_t* bitmap = sm + 64;            // ceil(S_max/32)
-  const int Wmax = (a.S_max + 31) >> 5;
-  uint32_t* skey = bitmap + Wmax;        // cap
+  const int Wmax = (((a.S_max + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
+  uint32_t* bitmap = sm + 64;            // positions with key > tau (16-byte aligned)
+  uint32_t* tbits = bitmap + Wmax;       // positions with key == tau
+  uint32_t* skey = tbits + Wmax;         // cap
   uint32_t* sidx = skey + cap_for(a.k);  // cap
 
   const int r = blockIdx.x;
@@ -194,11 +196,26 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   const bool direct = total > cap_for(a.k);
   const float* row = a.scores + (long long)r * a.ld;
 
-  uint32_t tau, want, eq_total;
+  uint32_t tau, want;
   if (!direct) {
-    for (uint32_t i = tid; i < total; i += kFinThreads) {
-      skey[i] = w.ekey[i];
-      sidx[i] = w.eidx[i];
+    // candidates to LDS, eight loads in flight per thread
+    constexpr int kU = 8;
+    for (uint32_t i0 = 0; i0 < total; i0 += kU * kFinThreads) {
+      uint32_t kk[kU], ii[kU];
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const uint32_t i = i0 + j * kFinThreads + tid;
+        kk[j] = i < total ? w.ekey[i] : 0u;
+        ii[j] = i < total ? w.eidx[i] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kU; ++j) {
+        const uint32_t i = i0 + j * kFinThreads + tid;
+        if (i < total) {
+          skey[i] = kk[j];
+          sidx[i] = ii[j];
+        }
+      }
     }
     __syncthreads();
     // Entries with bin > b* are all taken; resolve the rest inside bin b*.
@@ -218,66 +235,35 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
         },
         tau, 32, want, whist, sm);
   }
-  // Count the copies of tau; if not all are taken, keep the `want` lowest
-  // positions among them (largest ~position first).
-  if (tid == 0) sm[8] = 0u;
-  __syncthreads();
-  {
-    uint32_t c = 0;
-    if (!direct) {
-      for (uint32_t i = tid; i < total; i += kFinThreads) c += (skey[i] == tau);
-    } else {
-      for (int e = tid; e < n; e += kFinThreads) c += (order_key(row[e]) == tau);
-    }
-    atomicAdd(&sm[8], c);
+  // Mark {key > tau} and, separately, the copies of tau; of the copies the
+  // `want` lowest positions are taken (want >= 1 by the selection).
+  const int W4 = (((n + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
+  for (int i = tid; i < W4; i += kFinThreads) {
+    bitmap[i] = 0u;
+    tbits[i] = 0u;
   }
-  __syncthreads();
-  eq_total = sm[8];
-  __syncthreads();
-  uint32_t cut = 0xFFFFFFFFu;  // positions <= cut among the ties are taken
-  if (want < eq_total) {
-    // the want lowest positions = the want largest of (top - position), top < 2^18
-    const uint32_t top = (uint32_t)kMaxS - 1u;
-    uint32_t inv = 0u;
-    uint32_t wv = want;
-    if (!direct) {
-      radix_select_desc<kFinThreads, kDigitBits>(
-          [&](auto f) {
-            for (uint32_t i = tid; i < total; i += kFinThreads)
-              if (skey[i] == tau) f(top - sidx[i]);
-          },
-          inv, 18, wv, whist, sm);
-    } else {
-      radix_select_desc<kFinThreads, kDigitBits>(
-          [&](auto f) {
-            for (int e = tid; e < n; e += kFinThreads)
-              if (order_key(row[e]) == tau) f(top - (uint32_t)e);
-          },
-          inv, 18, wv, whist, sm);
-    }
-    cut = top - inv;
-  }
-  const int W = (n + 31) >> 5;
-  for (int i = tid; i < W; i += kFinThreads) bitmap[i] = 0u;
   __syncthreads();
   if (!direct) {
     for (uint32_t i = tid; i < total; i += kFinThreads) {
       const uint32_t key = skey[i], p = sidx[i];
-      if (key > tau || (key == tau && p <= cut)) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+      if (key > tau) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+      else if (key == tau) atomicOr(&tbits[p >> 5], 1u << (p & 31));
     }
   } else {
     for (int e = tid; e < n; e += kFinThreads) {
       const uint32_t key = order_key(row[e]);
-      if (key > tau || (key == tau && (uint32_t)e <= cut)) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      if (key > tau) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      else if (key == tau) atomicOr(&tbits[e >> 5], 1u << (e & 31));
     }
   }
   __syncthreads();
-  const uint32_t written = min(bitmap_to_sorted<kFinThreads>(bitmap, n, out, (uint32_t)a.k, sm), (uint32_t)a.k);
-  for (int j = (int)written + tid; j < a.k; j += kFinThreads) out[j] = -1;
+  const uint32_t written = bitmap_select_emit<kFinThreads>(bitmap, tbits, n, want, out, (uint32_t)a.k, sm);
+  for (int j = (int)min(written, (uint32_t)a.k) + tid; j < a.k; j += kFinThreads) out[j] = -1;
 }
 
 size_t final_lds_bytes(int S_max, int k) {
-  return (((size_t)(kFinThreads / 64) << kDigitBits) + 64 + ((S_max + 31) >> 5) + 2 * cap_for(k)) * 4;
+  return (((size_t)(kFinThreads / 64) << kDigitBits) + 64 + 2 * (size_t)((((S_max + 31) >> 5) + 3) & ~3) +
+          2 * cap_for(k)) * 4;
 }
 
 }  // namespace
