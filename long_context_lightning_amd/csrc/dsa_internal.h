@@ -110,6 +110,44 @@ __device__ __forceinline__ void load_head_weights(const void* w, int w_is_bf16, 
   }
 }
 
+// ---------------------------------------------------------- async memory
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One global -> LDS copy of 16 bytes per active lane (global_load_lds_dwordx4,
+// address = uniform base + per-lane 32-bit offset): lane l's bytes land at
+// lds_base + 16*l.  Issued from asm so the compiler does not make later LDS
+// reads or its own memory waits depend on it (it cannot tell buffers apart
+// and would drain every copy in flight); completion is tracked by the
+// caller's explicit vmcnt waits and barriers.  gbase and lds_base must be
+// the same for every lane of the wave.  No register result.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved, but nothing else in these kernels uses it
+__device__ __forceinline__ void dma16_lds(const void* gbase, uint32_t voff, const void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);  // uniform
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// One global -> LDS copy of 4 bytes per active lane (lane l's word lands at
+// lds_base + 4*l); otherwise as dma16_lds.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4_lds(const void* gbase, uint32_t voff, const void* lds_base) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t*)lds_base);  // uniform
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// A 4-byte global store issued from asm: the compiler keeps no wait for it
+// (its data register is read at issue).  Visibility to later reads needs a
+// vmcnt wait (a workgroup fence gives one).
+__device__ __forceinline__ void store_u32_nowait(uint32_t* p, uint32_t v) {
+  asm volatile("global_store_dword %0, %1, off" ::"v"(p), "v"(v) : "memory");
+}
+
 // ------------------------------------------------------------ launch args
 
 struct IndexerArgs {

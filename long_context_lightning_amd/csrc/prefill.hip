@@ -6,9 +6,10 @@
 // HBM.  This kernel does exactly that on gfx950:
 //
 //  * A block owns 16 consecutive query rows of one sequence (two per wave)
-//    and walks the causal key range [0, max_pos] in 64-key tiles staged
-//    through LDS (double buffered; 144-byte padded rows so the MFMA B-operand
-//    reads of 16 different keys hit distinct banks).
+//    and walks the causal key range [0, max_pos] in 64-key tiles copied
+//    straight from global memory into LDS one tile ahead (double buffered;
+//    XOR-swizzled 16-byte chunks so the MFMA B-operand reads of consecutive
+//    keys hit distinct banks).
 //  * Scores: v_mfma_f32_16x16x128_f8f6f4 with the query rows' 64x128 fp8
 //    tiles held in registers; ReLU, per-head weight and the reduction over
 //    the 64 heads are fused on the MFMA result registers; the k-scale and
@@ -34,15 +35,23 @@ namespace dsa {
 namespace {
 
 constexpr int kRows = 16;         // query rows per block
-constexpr int kWaves = 8;         // two rows per wave
+constexpr int kWaves = 8;         // two waves per SIMD
+constexpr int kRowsPerWave = kRows / kWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr int kNK = 64;           // keys per tile
-constexpr int kKRS = 144;         // LDS stride of one 128-byte key row
 constexpr int kMaxK = 4096;
 
 __host__ __device__ inline int cand_cap(int k) {
   int extra = k / 2 > 1024 ? k / 2 : 1024;
   return (k + extra + 63) / 64 * 64;
+}
+
+// Wait until this wave's vector-memory operations (loads, stores, global ->
+// LDS copies) have completed, then barrier with the LDS traffic drained.
+// The wait is the builtin so the compiler knows nothing is outstanding.
+__device__ __forceinline__ void drain_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ v8i lds_load32(const unsigned char* p) {
@@ -80,16 +89,28 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 // Keeps the `want` best entries under (key desc, position asc), in the
 // original (position-ascending) order.  Returns tau, the smallest kept key
 // (0 if nothing was dropped).  `hist` is this wave's 256-word LDS area.
+// Every pass over the list keeps kU loads per lane in flight.
+constexpr int kU = 8;
 __device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int want, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
   const unsigned long long lt = (1ull << lane) - 1ull;
   if (n <= want) return 0u;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's candidate stores have landed
   wave_sync_mem();
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = lane; i < n; i += 64) {
-    const uint32_t u = ekey[i];
-    mn = min(mn, u);
-    mx = max(mx, u);
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t u[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      u[j] = i < n ? ekey[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (base + 64 * j + lane < n) {
+        mn = min(mn, u[j]);
+        mx = max(mx, u[j]);
+      }
   }
   mn = wave_min(mn);
   mx = wave_max(mx);
@@ -105,9 +126,17 @@ __device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int wan
       for (int i = lane; i < 256; i += 64) hist[i] = 0u;
       wave_sync_mem();
       const uint32_t hi = rem_bits >= 32 ? 0u : prefix >> rem_bits;
-      for (int i = lane; i < n; i += 64) {
-        const uint32_t u = ekey[i];
-        if ((rem_bits >= 32 ? 0u : u >> rem_bits) == hi) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+      for (int base = 0; base < n; base += 64 * kU) {
+        uint32_t u[kU];
+#pragma unroll
+        for (int j = 0; j < kU; ++j) {
+          const int i = base + 64 * j + lane;
+          u[j] = i < n ? ekey[i] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kU; ++j)
+          if (base + 64 * j + lane < n && (rem_bits >= 32 ? 0u : u[j] >> rem_bits) == hi)
+            atomicAdd(&hist[(u[j] >> shift) & dmask], 1u);
       }
       wave_sync_mem();
       const int d0 = 4 * (63 - lane);
@@ -142,28 +171,36 @@ __device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int wan
     }
     tau = prefix;
   }
-  // Stable in-place compaction: keep key > tau and the first `rem` copies of tau.
+  // Stable in-place compaction: keep key > tau and the first `rem` copies of
+  // tau.  Entries are read kU chunks of 64 ahead of the writes; writes never
+  // pass the reads (w <= i), so in-place is safe.
   int w = 0;
   uint32_t eq_seen = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    uint32_t u = 0, p = 0;
-    if (i < n) {
-      u = ekey[i];
-      p = eidx[i];
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t u[kU], p[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      u[j] = i < n ? ekey[i] : 0u;
+      p[j] = i < n ? eidx[i] : 0u;
     }
-    const bool eq = i < n && u == tau;
-    const unsigned long long eqb = __ballot(eq);
-    const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqb & lt);
-    const bool keep = i < n && (u > tau || (eq && eq_rank < rem));
-    const unsigned long long kb = __ballot(keep);
-    if (keep) {
-      const int slot = w + __popcll(kb & lt);
-      ekey[slot] = u;
-      eidx[slot] = p;
+    wave_sync_mem();  // all reads of these chunks are done before any write
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      const bool eq = i < n && u[j] == tau;
+      const unsigned long long eqb = __ballot(eq);
+      const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqb & lt);
+      const bool keep = i < n && (u[j] > tau || (eq && eq_rank < rem));
+      const unsigned long long kb = __ballot(keep);
+      if (keep) {
+        const int slot = w + __popcll(kb & lt);
+        ekey[slot] = u[j];
+        eidx[slot] = p[j];
+      }
+      w += __popcll(kb);
+      eq_seen += (uint32_t)__popcll(eqb);
     }
-    w += __popcll(kb);
-    eq_seen += (uint32_t)__popcll(eqb);
   }
   n = w;
   wave_sync_mem();
@@ -171,12 +208,16 @@ __device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int wan
 }
 
 __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kNK * kKRS];
+  constexpr int R = kRowsPerWave;
+  // K tiles: 128-byte rows, the 16-byte chunk ch of key j at slot ch ^ (j & 7)
+  // (the MFMA operand reads of 8 consecutive keys then hit distinct banks).
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kNK * kDI];
   __shared__ float ksc[2][kNK];
-  __shared__ uint32_t hist[kWaves][256];
+  __shared__ uint32_t hist[kWaves][256];  // per-wave compaction histograms
   __shared__ int need_compact;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const unsigned long long lt = (1ull << lane) - 1ull;
 
@@ -190,13 +231,13 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   const int t_base = b * a.q_len + i0;
   const int maxpos = L - a.q_len + i0 + nrows - 1;  // position of the last row
 
-  // This wave's two rows.
-  int rpos[2];
-  bool rvalid[2];
-  int rt[2];
+  // This wave's rows.
+  int rpos[R];
+  bool rvalid[R];
+  int rt[R];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const int ri = 2 * wave + rr;
+  for (int rr = 0; rr < R; ++rr) {
+    const int ri = __builtin_amdgcn_readfirstlane(R * wave + rr);
     rvalid[rr] = ri < nrows;
     rt[rr] = t_base + ri;
     rpos[rr] = rvalid[rr] ? L - a.q_len + i0 + ri : -1;
@@ -204,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
 
   if (maxpos + 1 <= k) {  // every row keeps all of its positions
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
+    for (int rr = 0; rr < R; ++rr) {
       if (!rvalid[rr]) continue;
       int32_t* out = idx_out + (size_t)rt[rr] * k;
       for (int j = lane; j < k; j += 64) out[j] = (j <= rpos[rr]) ? j : -1;
@@ -213,23 +254,28 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   }
 
   // Candidate lists of this wave's rows.
-  uint32_t* ekey[2];
-  uint32_t* eidx[2];
+  uint32_t* ekey[R];
+  uint32_t* eidx[R];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
+  for (int rr = 0; rr < R; ++rr) {
     uint32_t* base = static_cast<uint32_t*>(ws) + (size_t)(rt[rr] - a.row_begin) * 2 * cap;
     ekey[rr] = base;
     eidx[rr] = base + cap;
   }
-  int n[2] = {0, 0};
-  uint32_t theta[2] = {0u, 0u};  // below every real key: everything valid enters
+  int n[R];
+  uint32_t theta[R];  // below every real key: everything valid enters
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    n[rr] = 0;
+    theta[rr] = 0u;
+  }
 
   // Query fragments and head weights (heads 16m + 4g + i of the MFMA output rows).
   const uint8_t* qb8 = static_cast<const uint8_t*>(a.q);
-  v8i qf[2][4];
-  float wv[2][4][4];
+  v8i qf[R][4];
+  float wv[R][4][4];
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
+  for (int rr = 0; rr < R; ++rr) {
     const size_t t = (size_t)rt[rr];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -244,61 +290,66 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
     }
   }
 
-  // Key tile staging: thread tid moves 16 bytes (key tid/8, chunk tid%8).
+  // Key tiles are copied straight from global memory into LDS, one tile
+  // ahead: wave w moves keys 8w..8w+7 of a tile (lane l: key 8w + l/8, slot
+  // l%8); wave 0 also moves the tile's 64 k-scales.  Keys past the last
+  // row's position read that position's row (their scores are masked).
   const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (size_t)b * a.S_max * kDI;
   const float* ksb = a.k_scale ? a.k_scale + (size_t)b * a.S_max : nullptr;
   const int ntiles = (maxpos + kNK) / kNK;
-  const int st_key = tid >> 3, st_chunk = tid & 7;
-  v4i pre;
-  float pre_sc = 1.f;
-  auto fetch = [&](int ti) {
-    const int s = ti * kNK + st_key;
-    pre = (s <= maxpos) ? *reinterpret_cast<const v4i*>(kb8 + (size_t)s * kDI + 16 * st_chunk) : v4i{0, 0, 0, 0};
-    if (tid < kNK) {
-      const int s2 = ti * kNK + tid;
-      pre_sc = (ksb && s2 <= maxpos) ? ksb[s2] : 1.f;
-    }
-  };
-  auto stage = [&](int buf) {
-    *reinterpret_cast<v4i*>(&ktile[buf][st_key * kKRS + 16 * st_chunk]) = pre;
-    if (tid < kNK) ksc[buf][tid] = pre_sc;
+  static_assert(kNK == 8 * kWaves, "one 16-byte copy per lane per tile");
+  auto issue = [&](int ti, int buf) {
+    const int key = ti * kNK + 8 * wave + (lane >> 3);
+    const int kc = min(key, maxpos);
+    const uint32_t chunk = (uint32_t)((lane & 7) ^ (key & 7));
+    dma16_lds(kb8, (uint32_t)kc * kDI + 16u * chunk, &ktile[buf][8 * wave * kDI]);
+    if (wave == 0 && ksb) dma4_lds(ksb, 4u * (uint32_t)min(ti * kNK + lane, maxpos), &ksc[buf][0]);
   };
 
   if (tid == 0) need_compact = 0;
-  fetch(0);
-  stage(0);
-  __syncthreads();
+  if (!ksb && tid < 2 * kNK) ksc[tid / kNK][tid % kNK] = 1.f;
+  issue(0, 0);
+  drain_barrier();
 
   for (int ti = 0; ti < ntiles; ++ti) {
     const int buf = ti & 1;
     const int tile0 = ti * kNK;
-    if (ti + 1 < ntiles) fetch(ti + 1);
+    if (ti + 1 < ntiles) issue(ti + 1, buf ^ 1);
 
-    const bool act0 = rpos[0] >= tile0, act1 = rpos[1] >= tile0;
-    if (act0 || act1) {
-      float x[2][4];
+    if (rpos[0] >= tile0 || rpos[R - 1] >= tile0) {  // positions grow with rr
+      // Every row of the wave is computed (a row past its position only
+      // masks its scores below).  Per key block: the two B-operand reads,
+      // all eight MFMAs, then the ReLU / weight epilogue of both rows.
+      float x[R][4];
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const v8i kf = lds_load32(&ktile[buf][(16 * blk + c) * kKRS + 32 * g]);
+        const unsigned char* krow = &ktile[buf][(16 * blk + c) * kDI];
+        const int sw = c & 7;
+        const v4i lo = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * g) ^ sw));
+        const v4i hi = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * g + 1) ^ sw));
+        const v8i kf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        v4f d[R][4];
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
+        for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) d[rr][m] = mfma_fp8(qf[rr][m], kf);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
           float acc = 0.f;
-          if (rr == 0 ? act0 : act1) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const v4f d = mfma_fp8(qf[rr][m], kf);
+          for (int m = 0; m < 4; ++m)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc = fmaf(wv[rr][m][i], fmaxf(d[i], 0.f), acc);
-            }
-          }
+            for (int i = 0; i < 4; ++i) acc = fmaf(wv[rr][m][i], fmaxf(d[rr][m][i], 0.f), acc);
           x[rr][blk] = acc;
         }
+        __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);        // the B-operand reads
+        __builtin_amdgcn_sched_group_barrier(0x0008, 4 * R, 0);    // the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x0002, 64 * R, 0);   // the epilogue
       }
       const float ks = ksc[buf][lane];
       const int s = tile0 + lane;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        if (!(rr == 0 ? act0 : act1)) continue;
+      for (int rr = 0; rr < R; ++rr) {
         auto p01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[rr][0]), __float_as_uint(x[rr][1]), false, false);
         auto p23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[rr][2]), __float_as_uint(x[rr][3]), false, false);
         const float a01 = __uint_as_float(p01[0]) + __uint_as_float(p01[1]);
@@ -312,35 +363,42 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
         if (ball) {
           const int slot = n[rr] + __popcll(ball & lt);
           if (pred) {
-            ekey[rr][slot] = u;
-            eidx[rr][slot] = (uint32_t)s;
+            store_u32_nowait(ekey[rr] + slot, u);
+            store_u32_nowait(eidx[rr] + slot, (uint32_t)s);
           }
           n[rr] += __popcll(ball);
         }
       }
-      if (lane == 0 && (n[0] > cap - kNK || n[1] > cap - kNK)) atomicOr(&need_compact, 1);
+      bool full = false;
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) full = full || n[rr] > cap - kNK;
+      if (lane == 0 && full) atomicOr(&need_compact, 1);
     }
 
-    if (ti + 1 < ntiles) stage(buf ^ 1);
-    __syncthreads();
+    // This wave's copies of tile ti+1 (and its candidate stores) are done;
+    // after the barrier every wave's are, and tile ti is free.
+    drain_barrier();
     if (need_compact) {
       // Batched: every wave trims its fuller lists so compactions overlap.
       const int trigger = k + (cap - k) / 2;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
+      for (int rr = 0; rr < R; ++rr)
         if (n[rr] > trigger) {
           const uint32_t tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
           theta[rr] = tau;
         }
       __syncthreads();
       if (tid == 0) need_compact = 0;
+      // nothing of the compaction stays in flight into the next tile (the
+      // compiler would otherwise wait for it inside the MFMA sequence)
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
 
   // Final exact selection and output (ascending positions, -1 padded).
 #pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
+  for (int rr = 0; rr < R; ++rr) {
     if (!rvalid[rr]) continue;
     int32_t* out = idx_out + (size_t)rt[rr] * k;
     if (rpos[rr] + 1 <= k) {

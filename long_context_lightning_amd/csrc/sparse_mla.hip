@@ -75,20 +75,6 @@ __device__ __forceinline__ void vm_wait(int n) {
 // drain the vector-memory counter and stall the gather ring.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// One global -> LDS copy of 16 bytes per active lane (global_load_lds_dwordx4,
-// address = uniform base + per-lane 32-bit offset): lane l's bytes land at
-// lds_base + 16*l.  Issued from asm so the compiler does not make every later
-// LDS read wait for it (it cannot tell the ring slots apart and would drain
-// the whole ring); completion is tracked by vm_wait and the ring barrier.
-// The instruction has no register result.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved, but nothing else in these kernels uses it
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* lds_base) {
-  const uint32_t m = (uint32_t)(uintptr_t)(const lds_void*)lds_base;
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // Partition of one row's k indices into splits of whole tiles.
 __host__ __device__ inline int mla_splits(int T, int k) {
@@ -152,13 +138,13 @@ __device__ __forceinline__ void gather_tile(const TileSrc& src, int mb, unsigned
   const int row0 = wave * kRowsPerWave;
 #pragma unroll
   for (int rr = 0; rr < kRowsPerWave; ++rr)
-    dma16(src.kvb + (size_t)sidx[rr] * kDQK, 16u * lane, tile + (row0 + rr) * kMainRS);
+    dma16_lds(src.kvb + (size_t)sidx[rr] * kDQK, 16u * lane, tile + (row0 + rr) * kMainRS);
   // rope pieces: lane l < 32 -> row row0 + l/8, slot l%8
   const int rr = (lane >> 3) & 3;
   const int s = rr == 0 ? sidx[0] : rr == 1 ? sidx[1] : rr == 2 ? sidx[2] : sidx[3];
   const int piece = 64 + ((lane & 7) ^ ((row0 + rr) & 7));
   if (lane < 8 * kRowsPerWave)
-    dma16(src.kvb, (uint32_t)s * (2 * kDQK) + 16u * piece, tile + kMainBytes + row0 * kRopeRS);
+    dma16_lds(src.kvb, (uint32_t)s * (2 * kDQK) + 16u * piece, tile + kMainBytes + row0 * kRopeRS);
 }
 
 // FULL: H is a multiple of 32, so a wave's second 16-head block exists
