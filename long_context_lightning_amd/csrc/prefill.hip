@@ -42,7 +42,7 @@ constexpr int kNK = 64;           // keys per tile
 constexpr int kMaxK = 4096;
 
 __host__ __device__ inline int cand_cap(int k) {
-  int extra = k / 2 > 1024 ? k / 2 : 1024;
+  int extra = k > 1024 ? k : 1024;
   return (k + extra + 63) / 64 * 64;
 }
 
@@ -84,6 +84,15 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
   return v;
 }
+
+// Threshold-only compaction of one row's candidate list by one wave: one
+// histogram pass over the 8 key bits below the list's common prefix finds
+// the bin holding the want-th largest key; every entry at or above that
+// bin's floor tau is kept (at least `want` of them), the rest dropped, in
+// the original order.  No dropped entry can be among the final top `want`,
+// and a later key can only enter if it is > tau: with >= want kept entries
+// at or above tau, a later key equal to tau loses on position.  Returns tau.
+__device__ uint32_t wave_trim(uint32_t* ekey, uint32_t* eidx, int& n, int want, uint32_t* hist);
 
 // Exact compaction of one row's candidate list by one wave.
 // Keeps the `want` best entries under (key desc, position asc), in the
@@ -207,6 +216,101 @@ __device__ uint32_t wave_compact(uint32_t* ekey, uint32_t* eidx, int& n, int wan
   return tau;
 }
 
+__device__ uint32_t wave_trim(uint32_t* ekey, uint32_t* eidx, int& n, int want, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  if (n <= want) return 0u;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's candidate stores have landed
+  wave_sync_mem();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t u[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      u[j] = i < n ? ekey[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (base + 64 * j + lane < n) {
+        mn = min(mn, u[j]);
+        mx = max(mx, u[j]);
+      }
+  }
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (mn == mx) return 0u;  // all keys equal: nothing can be dropped by key
+  const int rem_bits = 32 - __clz(mn ^ mx);
+  const int nb = rem_bits < 8 ? rem_bits : 8;
+  const int shift = rem_bits - nb;
+  const uint32_t dmask = (1u << nb) - 1u;
+  const uint32_t prefix = rem_bits >= 32 ? 0u : (mn & (0xFFFFFFFFu << rem_bits));
+  for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+  wave_sync_mem();
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t u[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      u[j] = i < n ? ekey[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j)
+      if (base + 64 * j + lane < n) atomicAdd(&hist[(u[j] >> shift) & dmask], 1u);
+  }
+  wave_sync_mem();
+  const int d0 = 4 * (63 - lane);
+  uint32_t c[4], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    c[j] = hist[d0 + 3 - j];
+    tot += c[j];
+  }
+  const uint32_t rem = (uint32_t)want;
+  const uint32_t above = wave_inclusive_sum(tot) - tot;
+  uint32_t dsel = 0;
+  const bool mine = above < rem && rem <= above + tot;
+  if (mine) {
+    uint32_t acc = above;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (acc < rem && rem <= acc + c[j]) dsel = (uint32_t)(d0 + 3 - j);
+      acc += c[j];
+    }
+  }
+  const unsigned long long who = __ballot(mine);
+  const int src = __ffsll((long long)who) - 1;
+  dsel = (uint32_t)__shfl((int)dsel, src, 64);
+  const uint32_t tau = prefix | (dsel << shift);  // floor of the bin holding the want-th key
+  wave_sync_mem();
+  int w = 0;
+  for (int base = 0; base < n; base += 64 * kU) {
+    uint32_t u[kU], p[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      u[j] = i < n ? ekey[i] : 0u;
+      p[j] = i < n ? eidx[i] : 0u;
+    }
+    wave_sync_mem();  // all reads of these chunks are done before any write
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int i = base + 64 * j + lane;
+      const bool keep = i < n && u[j] >= tau;
+      const unsigned long long kb = __ballot(keep);
+      if (keep) {
+        const int slot = w + __popcll(kb & lt);
+        ekey[slot] = u[j];
+        eidx[slot] = p[j];
+      }
+      w += __popcll(kb);
+    }
+  }
+  n = w;
+  wave_sync_mem();
+  return tau;
+}
+
 __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
   constexpr int R = kRowsPerWave;
   // K tiles: 128-byte rows, the 16-byte chunk ch of key j at slot ch ^ (j & 7)
@@ -306,6 +410,23 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
     if (wave == 0 && ksb) dma4_lds(ksb, 4u * (uint32_t)min(ti * kNK + lane, maxpos), &ksc[buf][0]);
   };
 
+  // A tile's accepted candidates are stored at the start of the next tile
+  // (next to that tile's copy), so the end-of-tile wait finds both long done.
+  bool pend[R];
+  uint32_t pu[R], ps[R];
+  int pslot[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) pend[rr] = false;
+  auto flush = [&]() {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+      if (pend[rr]) {
+        store_u32_nowait(ekey[rr] + pslot[rr], pu[rr]);
+        store_u32_nowait(eidx[rr] + pslot[rr], ps[rr]);
+        pend[rr] = false;
+      }
+  };
+
   if (tid == 0) need_compact = 0;
   if (!ksb && tid < 2 * kNK) ksc[tid / kNK][tid % kNK] = 1.f;
   issue(0, 0);
@@ -315,6 +436,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
     const int buf = ti & 1;
     const int tile0 = ti * kNK;
     if (ti + 1 < ntiles) issue(ti + 1, buf ^ 1);
+    flush();
 
     if (rpos[0] >= tile0 || rpos[R - 1] >= tile0) {  // positions grow with rr
       // Every row of the wave is computed (a row past its position only
@@ -360,14 +482,11 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
         const bool valid = s <= rpos[rr];
         const bool pred = valid && u > theta[rr];
         const unsigned long long ball = __ballot(pred);
-        if (ball) {
-          const int slot = n[rr] + __popcll(ball & lt);
-          if (pred) {
-            store_u32_nowait(ekey[rr] + slot, u);
-            store_u32_nowait(eidx[rr] + slot, (uint32_t)s);
-          }
-          n[rr] += __popcll(ball);
-        }
+        pend[rr] = pred;
+        pu[rr] = u;
+        ps[rr] = (uint32_t)s;
+        pslot[rr] = n[rr] + __popcll(ball & lt);
+        n[rr] += __popcll(ball);
       }
       bool full = false;
 #pragma unroll
@@ -379,13 +498,17 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
     // after the barrier every wave's are, and tile ti is free.
     drain_barrier();
     if (need_compact) {
-      // Batched: every wave trims its fuller lists so compactions overlap.
+      flush();
+      // Batched: every wave trims its fuller lists so the trims overlap.
+      // A trim keeps the keys at or above a threshold (>= k entries); if
+      // that would leave the list nearly full, the exact compaction runs.
       const int trigger = k + (cap - k) / 2;
 #pragma unroll
       for (int rr = 0; rr < R; ++rr)
         if (n[rr] > trigger) {
-          const uint32_t tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
-          theta[rr] = tau;
+          uint32_t tau = wave_trim(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+          if (n[rr] > trigger) tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+          theta[rr] = max(theta[rr], tau);
         }
       __syncthreads();
       if (tid == 0) need_compact = 0;
@@ -395,6 +518,8 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
       __syncthreads();
     }
   }
+
+  flush();
 
   // Final exact selection and output (ascending positions, -1 padded).
 #pragma unroll
