@@ -85,8 +85,17 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_hist(TopkArgs a) {
   __syncthreads();
   const float* row = a.scores + (long long)r * a.ld;
   const int e1 = min(seg0 + kSeg, n);
-  for (int e = seg0 + (int)threadIdx.x; e < e1; e += kSegThreads)
-    atomicAdd(&h[order_key(row[e]) >> kBinShift], 1u);
+  // all loads first (addresses clamped into the segment, so no branches)
+  constexpr int kPer = kSeg / kSegThreads;
+  uint32_t key[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = seg0 + (int)threadIdx.x + j * kSegThreads;
+    key[j] = order_key(row[e < e1 ? e : e1 - 1]);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (seg0 + (int)threadIdx.x + j * kSegThreads < e1) atomicAdd(&h[key[j] >> kBinShift], 1u);
   __syncthreads();
   RowWs w = row_ws(a.ws, r, a.k);
   for (int i = threadIdx.x; i < kBins; i += kSegThreads)
@@ -138,19 +147,25 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
   const int n = row_valid_count(a, r);
   const int seg0 = (int)blockIdx.x * kSeg;
   if (n <= a.k || seg0 >= n) return;
+  const float* row = a.scores + (long long)r * a.ld;
+  const int e1 = min(seg0 + kSeg, n);
+  // Keys of this thread's scores stay in registers (all loads issued first,
+  // addresses clamped into the segment, before the threshold search so the
+  // two overlap); one reservation per block.
+  uint32_t key[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = seg0 + (int)threadIdx.x + j * kSegThreads;
+    key[j] = order_key(row[e < e1 ? e : e1 - 1]);
+  }
   RowWs w = row_ws(a.ws, r, a.k);
   uint32_t bstar, above;
   find_threshold_bin<kSegThreads>(w.hist, (uint32_t)a.k, sm, &bstar, &above);
   if ((size_t)above + w.hist[bstar] > cap_for(a.k)) return;  // final block takes the direct path
-  const float* row = a.scores + (long long)r * a.ld;
-  const int e1 = min(seg0 + kSeg, n);
-  // Keys of this thread's scores stay in registers; one reservation per block.
-  uint32_t key[kPer];
   uint32_t mine = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = seg0 + (int)threadIdx.x + j * kSegThreads;
-    key[j] = e < e1 ? order_key(row[e]) : 0u;
     mine += (e < e1 && (key[j] >> kBinShift) >= bstar) ? 1u : 0u;
   }
   uint32_t total;
