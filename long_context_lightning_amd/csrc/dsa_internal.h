@@ -130,6 +130,22 @@ __device__ __forceinline__ void dma16_lds(const void* gbase, uint32_t voff, cons
 }
 #pragma clang diagnostic pop
 
+// As dma16_lds, but from a per-lane 64-bit address, into the LDS byte offset
+// lds_off (the same for every lane of the wave).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_lds_at(const void* gaddr, uint32_t lds_off) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS byte offset of a __shared__ object (its address in the LDS aperture).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
 // One global -> LDS copy of 4 bytes per active lane (lane l's word lands at
 // lds_base + 4*l); otherwise as dma16_lds.
 #pragma clang diagnostic push

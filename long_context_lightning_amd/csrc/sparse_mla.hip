@@ -6,24 +6,28 @@
 // value its first 512 dims; the softmax covers the selected rows only.
 //
 // bf16 path.  A block owns one query row, one contiguous slice (split) of its
-// selected indices and all H heads, with 8 waves, two per SIMD.  Heads come
-// in groups of 32; the two waves of a group split the latent dims between
-// them: wave half 0 takes score dims 0..287 and value dims 0..255, half 1
-// the rest.  The selected rows are gathered 32 at a time (1152 bytes each, in
-// 16-byte pieces, straight from global memory into LDS) through a ring of
-// three padded tiles, so two tiles are in flight while one computes.
-// Per tile and wave:
-//   partial S^T[32 keys x 32 heads] = K_tile[32 x 288] . Q^T[288 x 32]
-//     (9 K-steps of v_mfma_f32_16x16x32_bf16 per 16-head block; the Q^T
-//     fragments live in registers);
-//   the two halves swap their partial scores through LDS and add them, so
-//     both hold the same full scores and the same softmax weights;
-//   softmax in fp32 with base-2 exponents, lane <-> head;
-//   O^T[256 dims x 32 heads] += V^T[256 x 32 keys] . P^T[32 keys x 32 heads]:
+// selected indices and all H heads, with 4 waves, one per SIMD (each wave has
+// the SIMD's whole register file: 256 VGPRs plus 256 AGPRs).  The selected
+// rows are gathered 32 at a time (1152 bytes each, in 16-byte pieces,
+// straight from global memory into LDS) through a ring of three padded tiles,
+// so two tiles are in flight while one computes.  Per tile:
+//   scores: wave w takes heads 32w..32w+31 over all 576 dims,
+//     S^T[32 keys x 32 heads] = K_tile[32 x 576] . Q^T[576 x 32]
+//     (18 K-steps of v_mfma_f32_16x16x32_bf16 per 16-head block; each K
+//     fragment read from LDS feeds both head blocks; the Q^T fragments live in
+//     registers), then the softmax weights of those heads in fp32 with base-2
+//     exponents, lane <-> head, rounded to bf16 and written to a shared
+//     P[head][key] buffer in LDS;
+//   values: wave w takes value dims 128w..128w+127 for all heads,
+//     O^T[128 dims x 128 heads] += V^T[128 x 32 keys] . P^T[32 keys x 128 heads]:
 //     V^T is read with the gfx950 LDS transpose load (ds_read_b64_tr_b16)
-//     straight from the row-major tile; P^T is already in the right
-//     registers because the score rows of lane row g are keys 4g..4g+3 and
-//     16+4g..16+4g+3.
+//     straight from the row-major tile, and every V^T fragment feeds all
+//     eight head blocks, so each tile is read from LDS once for the scores'
+//     K fragments per head pair and once for the values.  The accumulators
+//     (256 per lane) stay in AGPRs.
+// Keys inside a P row are stored in the order the MFMA contracts them: lane
+// row g of a score block holds keys 4g..4g+3 and 16+4g..16+4g+3, which is
+// the k-slice 8g..8g+7 of the value product.
 // With one split the block writes the bf16 output and the log-sum-exp; with
 // several each split writes its bf16 output normalised by its own sum plus
 // (max, sum), and a combine kernel merges them.
@@ -38,22 +42,26 @@ constexpr int kMainRS = 1056;                    // LDS stride of a row's dims 0
 constexpr int kMainBytes = kNT * kMainRS;        // 33792
 constexpr int kRopeRS = 128;                     // dims 512..575 of a row: 8 pieces, XOR-swizzled
 constexpr int kTileBytes = kMainBytes + kNT * kRopeRS;  // 37888
-constexpr int kWaves = 8;                        // 4 head groups x 2 dim halves
+constexpr int kWaves = 4;                        // one per SIMD
+constexpr int kSlots = 4;                        // ring slots: values, scores, two tiles in flight
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = kNT / kWaves;       // rows of a tile gathered by each wave (4)
+constexpr int kRowsPerWave = kNT / kWaves;       // rows of a tile gathered by each wave (8)
 constexpr int kDma = kRowsPerWave + 1;           // gather instructions per wave per tile
-constexpr int kKsMain = 8;                       // score K-steps per wave over dims 0..511
-constexpr int kKsHalf = kKsMain + 1;             // ... plus one over the rope dims 512..575
-constexpr int kDbHalf = kDV / 16 / 2;            // 16-dim value blocks per wave (16)
+constexpr int kKs = kDQK / 32;                   // score K-steps: 16 over dims 0..511, 2 over the rope dims
+constexpr int kKsMain = kDV / 32;
+constexpr int kMaxHB = 8;                        // 16-head blocks (H <= 128)
+constexpr int kDbW = kDV / 16 / kWaves;          // 16-dim value blocks per wave (8)
+constexpr int kPRow = 2 * kNT;                   // bytes of one head's P row (32 keys, bf16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-static_assert(kRowsPerWave * 8 <= 64, "one instruction moves the rope pieces of a wave's rows");
+static_assert(kRowsPerWave * 8 == 64, "one instruction moves the rope pieces of a wave's rows");
+static_assert(kKs == kKsMain + 2, "two rope K-steps");
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int v8i_a4 __attribute__((ext_vector_type(8), aligned(4)));
 
 __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -61,13 +69,20 @@ __device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
 
 __device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
 
-// Wait until at most n (0 or kDma) of this wave's vector-memory operations are in flight.
-__device__ __forceinline__ void vm_wait(int n) {
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
   // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
-  if (n >= kDma)
-    __builtin_amdgcn_s_waitcnt((kDma & 15) | ((kDma >> 4) << 14) | 0x70 | 0xF00);
-  else
-    __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// vm_wait for the counts the prologue can leave in flight.
+__device__ __forceinline__ void vm_wait_n(int n) {
+  if (n >= 2 * kDma + 1) vm_wait<2 * kDma + 1>();
+  else if (n >= 2 * kDma) vm_wait<2 * kDma>();
+  else if (n >= kDma) vm_wait<kDma>();
+  else vm_wait<0>();
 }
 
 // Block barrier that leaves vector-memory operations in flight: LDS traffic
@@ -103,63 +118,127 @@ __device__ __forceinline__ Partials partials(const MlaArgs& a, int ns) {
   return p;
 }
 
-// Gather of one tile: wave w moves tile rows 4w..4w+3 straight into LDS,
+// Gather of one tile: wave w moves tile rows 8w..8w+7 straight into LDS,
 // 16 bytes per lane per instruction: one instruction per row for its dims
-// 0..511 (64 pieces, row stride kMainRS), and one more whose first 32 lanes
-// move the rope pieces (dims 512..575) of the four rows.  Rope piece p of
-// row r sits at position p ^ (r & 7) of the row's 128-byte slot, so the
-// score reads of 8 consecutive rows hit distinct banks.  Rows past the split
-// or not selectable read row 0 of the sequence (a real row whenever the query
-// sees any key), so every instruction is issued with the same lanes and the
-// wait counts stay exact; the row's validity bit masks its score.
+// 0..511 (64 pieces, row stride kMainRS), and one more that moves the rope
+// pieces (dims 512..575) of the eight rows.  Rope piece p of row r sits at
+// position p ^ ((r >> 1) & 7) of the row's 128-byte slot: two consecutive
+// rows share a 256-byte bank line, so the 16 rows one score read covers
+// (16 lanes x 16 bytes per LDS cycle) fall on distinct banks.  Rows past the split or not
+// selectable read row 0 of the sequence (a real row whenever the query sees
+// any key), so every instruction is issued with the same lanes and the wait
+// counts stay exact; the row's validity bit masks its score.
 struct TileSrc {
   const uint16_t* kvb;
   const int32_t* idx_row;
   int m1, pos;
 };
 
-__device__ __forceinline__ void gather_tile(const TileSrc& src, int mb, unsigned char* tile, unsigned char* vmask,
-                                            int wave, int lane) {
-  // The indices are wave-uniform: read them with scalar loads so they never
-  // enter the vector-memory counter the tile waits are counted on.
-  int sidx[kRowsPerWave];
-  uint32_t vbits = 0;
-#pragma unroll
-  for (int rr = 0; rr < kRowsPerWave; ++rr) {
-    const int m = __builtin_amdgcn_readfirstlane(mb + wave * kRowsPerWave + rr);
-    const int mc = m < src.m1 ? m : src.m1 - 1;
-    int s = __builtin_amdgcn_readfirstlane(src.idx_row[mc]);
-    s = m < src.m1 ? s : -1;
-    const bool ok = s >= 0 && s <= src.pos;
-    sidx[rr] = ok ? s : 0;
-    vbits |= (ok ? 1u : 0u) << rr;
+// The gather of one tile in steps, so the tile loop can spread them over
+// the score MFMAs of the tile before (their issue costs then overlap matrix
+// work): the wave's eight indices (from LDS, or from a scalar load before the
+// loop), their validity, then one instruction per row and the rope one.
+struct TileGather {
+  v4i lo, hi;                 // raw indices of rows 0..3 / 4..7 (the same in every lane)
+  int sidx[kRowsPerWave];     // rows to read (0 for invalid ones), held per lane
+  int rope_s;                 // this lane's row of the rope instruction
+  uint32_t lane16;            // 16 * lane, made opaque per tile so no per-row address is hoisted
+
+  __device__ __forceinline__ void read_lds(const int32_t* slot) {
+    lo = *reinterpret_cast<const v4i*>(slot);
+    hi = *reinterpret_cast<const v4i*>(slot + 4);
   }
-  if (lane == 0) vmask[wave] = (unsigned char)vbits;  // byte w: validity of rows 4w..4w+3
-  const int row0 = wave * kRowsPerWave;
+  // Validity of the wave's rows (entries at or past the split end, negative
+  // or past the query position are invalid), computed per lane on vectors so
+  // no scalar chain sits in the issue stream.
+  __device__ __forceinline__ void decode(const TileSrc& src, int mb, unsigned char* vmask, int wave, int lane) {
+    const int mw = mb + wave * kRowsPerWave;
+    uint32_t vbits = 0;
 #pragma unroll
-  for (int rr = 0; rr < kRowsPerWave; ++rr)
-    dma16_lds(src.kvb + (size_t)sidx[rr] * kDQK, 16u * lane, tile + (row0 + rr) * kMainRS);
-  // rope pieces: lane l < 32 -> row row0 + l/8, slot l%8
-  const int rr = (lane >> 3) & 3;
-  const int s = rr == 0 ? sidx[0] : rr == 1 ? sidx[1] : rr == 2 ? sidx[2] : sidx[3];
-  const int piece = 64 + ((lane & 7) ^ ((row0 + rr) & 7));
-  if (lane < 8 * kRowsPerWave)
-    dma16_lds(src.kvb, (uint32_t)s * (2 * kDQK) + 16u * piece, tile + kMainBytes + row0 * kRopeRS);
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+      const int raw = rr < 4 ? lo[rr] : hi[rr - 4];
+      const bool ok = mw + rr < src.m1 && raw >= 0 && raw <= src.pos;
+      sidx[rr] = ok ? raw : 0;
+      vbits |= (ok ? 1u : 0u) << rr;
+    }
+    if (lane == 0) vmask[wave] = (unsigned char)vbits;  // byte w: validity of rows 8w..8w+7
+    lane16 = 16u * (uint32_t)lane;
+    asm volatile("" : "+v"(lane16));
+    const int rr = lane >> 3;
+    rope_s = sidx[0];
+#pragma unroll
+    for (int j = 1; j < kRowsPerWave; ++j) rope_s = rr == j ? sidx[j] : rope_s;
+  }
+  // dims 0..511 of tile row 8w + rr: 64 pieces, one per lane (per-lane
+  // address: one multiply-add per row)
+  __device__ __forceinline__ void row(const TileSrc& src, int rr, uint32_t tile, int wave, int lane) const {
+    const char* rowp = reinterpret_cast<const char*>(src.kvb) + (size_t)sidx[rr] * (2 * kDQK);
+    dma16_lds_at(rowp + lane16, tile + (wave * kRowsPerWave + rr) * kMainRS);
+  }
+  // rope pieces: lane l -> row 8w + l/8, slot l%8
+  __device__ __forceinline__ void rope(const TileSrc& src, uint32_t tile, int wave, int lane) const {
+    const int row0 = wave * kRowsPerWave;
+    const int piece = 64 + ((lane & 7) ^ (((row0 + (lane >> 3)) >> 1) & 7));
+    dma16_lds_at(src.kvb + (size_t)rope_s * kDQK + 8 * piece, tile + kMainBytes + row0 * kRopeRS);
+  }
+  __device__ __forceinline__ void all_rows(const TileSrc& src, uint32_t tile, int wave, int lane) const {
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) row(src, rr, tile, wave, lane);
+    rope(src, tile, wave, lane);
+  }
+};
+
+// Indices read by scalar loads (used before the tile loop, so they stay off
+// the vector-memory counter; a wave's eight indices are contiguous: one
+// 32-byte load unless the split ends inside them).
+__device__ __forceinline__ TileGather scalar_indices(const TileSrc& src, int mb, int wave) {
+  const int mw = __builtin_amdgcn_readfirstlane(mb + wave * kRowsPerWave);
+  int raw[kRowsPerWave];
+  if (mw + kRowsPerWave <= src.m1) {
+    const v8i_a4 v = *reinterpret_cast<const v8i_a4*>(src.idx_row + mw);
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) raw[rr] = __builtin_amdgcn_readfirstlane(v[rr]);
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < kRowsPerWave; ++rr) {
+      const int m = mw + rr;
+      raw[rr] = __builtin_amdgcn_readfirstlane(src.idx_row[m < src.m1 ? m : src.m1 - 1]);
+    }
+  }
+  TileGather tg;
+  tg.lo = v4i{raw[0], raw[1], raw[2], raw[3]};
+  tg.hi = v4i{raw[4], raw[5], raw[6], raw[7]};
+  return tg;
 }
 
-// FULL: H is a multiple of 32, so a wave's second 16-head block exists
-// whenever its first does.
-template <bool FULL>
+// Inside the tile loop the indices arrive one tile ahead, by a 4-byte
+// global -> LDS copy of the wave's eight entries (clamped into the split),
+// so no scalar-load latency sits in front of a gather.
+__device__ __forceinline__ void fetch_indices(const TileSrc& src, int mb, int32_t* slot, int wave, int lane) {
+  if (lane < kRowsPerWave) {
+    const int m = mb + wave * kRowsPerWave + lane;
+    dma4_lds(src.idx_row, 4u * (uint32_t)(m < src.m1 ? m : src.m1 - 1), slot);
+  }
+}
+
+
+// NHB = H / 16 head blocks: wave w runs the softmax of blocks 2w and 2w+1
+// (those below NHB), and every wave's value product covers all NHB.
+template <int NHB>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32_t* __restrict__ idx, int ns,
                                                         int per_split, int per_xcd) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[3 * kTileBytes];
-  __shared__ v4f xbuf[kWaves][4][64];  // partial scores swapped between the two halves of a head group
-  __shared__ uint64_t vmask[3];  // per ring slot: byte w = validity bits of tile rows 4w..4w+3
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kSlots * kTileBytes];
+  // P[head][key] bf16; the 16-byte chunk j of head h's row sits at position
+  // j ^ ((h >> 2) & 3), so 16 consecutive heads read or written at one chunk
+  // fall on distinct banks.
+  __shared__ __attribute__((aligned(16))) unsigned char pbuf[kMaxHB * 16 * kPRow];
+  __shared__ uint32_t vmask[kSlots];  // per ring slot: bit r = validity of tile row r
+  __shared__ __attribute__((aligned(16))) int32_t islot[kWaves][4][kRowsPerWave];  // prefetched row indices
+  __shared__ float hinv[kMaxHB * 16];
   __shared__ int overflow_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave & 3, half = wave >> 2;
   const int g = lane >> 4, c = lane & 15;
   // Blocks go round-robin over the 8 XCDs; give each XCD whole queries so the
   // splits of one query share that XCD's L2 (its query rows are read once).
@@ -173,43 +252,66 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   const int m1 = min(a.k, m0 + per_split);
   // a query that sees no key gathers nothing (its output is zero)
   const int ntiles = (m1 > m0 && pos >= 0) ? (m1 - m0 + kNT - 1) / kNT : 0;
-  const int h0 = 32 * grp;
-  const bool hb0 = h0 < a.H;                               // this wave has heads
-  const bool hb1 = FULL ? hb0 : (h0 + 16 < a.H);           // ... and a second 16-head block
+  const bool sh0 = NHB >= 2 * kWaves - 1 || 2 * wave < NHB;  // this wave has score heads
+  const bool sh1 = NHB >= 2 * kWaves || 2 * wave + 1 < NHB;   // ... and a second 16-head block
 
   // Per-lane LDS offsets within a tile (kept as single opaque values so the
-  // compiler neither splits nor re-derives them inside the tile loop):
-  // score-read row c of key block 0 (dims 0..511 and rope part) and the V^T
-  // transpose-read position.
-  int aoff = c * kMainRS + 16 * g + 512 * half;
-  int roff = kMainBytes + c * kRopeRS + 16 * ((4 * half + g) ^ (c & 7));
-  int voff = (4 * g + (c >> 2)) * kMainRS + 8 * (c & 3) + 32 * kDbHalf * half;
-  asm volatile("" : "+v"(aoff), "+v"(roff), "+v"(voff));
+  // compiler neither splits nor re-derives them inside the tile loop): score
+  // read of row c over dims 0..511 and over the two rope K-steps, V^T
+  // transpose-read position of this wave's value dims, and the P read.
+  int aoff = c * kMainRS + 16 * g;
+  int roff0 = kMainBytes + c * kRopeRS + 16 * (g ^ ((c >> 1) & 7));
+  int roff1 = roff0 ^ 64;  // rope piece 4 + g: slot (g ^ ((c >> 1) & 7)) ^ 4
+  int voff = (4 * g + (c >> 2)) * kMainRS + 8 * (c & 3) + 2 * (kDV / kWaves) * wave;
+  int poff = c * kPRow + 16 * (g ^ ((c >> 2) & 3));
+  asm volatile("" : "+v"(aoff), "+v"(roff0), "+v"(roff1), "+v"(voff), "+v"(poff));
 
   TileSrc src;
   src.kvb = static_cast<const uint16_t*>(a.kv) + (size_t)b * a.S_max * kDQK;
   src.idx_row = idx + (size_t)t * a.k;
   src.m1 = m1;
   src.pos = pos;
+  unsigned char* const vmb = reinterpret_cast<unsigned char*>(vmask);
+  const uint32_t ring_off = lds_offset(ring);
 
-  // The first two tiles, then the Q^T fragments; the Q load overlaps the
-  // gathers.  Lane holds head h0 + 16*hb + c, dims 32*(8*half + i) + 8g .. +7
-  // for i < 8 and rope dims 32*(16 + half) + 8g .. +7 for i = 8.
-  if (ntiles > 0) gather_tile(src, m0, ring, reinterpret_cast<unsigned char*>(&vmask[0]), wave, lane);
-  if (ntiles > 1) gather_tile(src, m0 + kNT, ring + kTileBytes, reinterpret_cast<unsigned char*>(&vmask[1]), wave, lane);
-  v8bf qf[2][kKsHalf];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const bool on = hb ? hb1 : hb0;
-    const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + (on ? h0 + 16 * hb + c : 0)) * kDQK + 8 * g;
-#pragma unroll
-    for (int i = 0; i < kKsHalf; ++i) {
-      const int ks = i < kKsMain ? kKsMain * half + i : 2 * kKsMain + half;
-      qf[hb][i] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
+  // Copies before the loop, in this order per wave: tile 0 (kDma), the Q^T
+  // fragments (kQLoads), tile 1 (kDma), the indices of tile 3 (1), tile 2
+  // (kDma).  The scores of tile 0 wait for tile 0 and Q only (the later
+  // copies stay in flight).
+  // Lane holds head 16*(2w + j) + c, dims 32*ks + 8g .. +7.
+  TileGather g1, g2;
+  auto prologue = [&]() {
+    TileGather g0 = scalar_indices(src, m0, wave);
+    if (ntiles > 1) g1 = scalar_indices(src, m0 + kNT, wave);
+    if (ntiles > 2) g2 = scalar_indices(src, m0 + 2 * kNT, wave);
+    if (ntiles > 0) {
+      g0.decode(src, m0, vmb, wave, lane);
+      g0.all_rows(src, ring_off, wave, lane);
     }
+  };
+  auto prologue_rest = [&]() {
+    if (ntiles > 1) {
+      g1.decode(src, m0 + kNT, vmb + 4, wave, lane);
+      g1.all_rows(src, ring_off + kTileBytes, wave, lane);
+    }
+    if (ntiles > 3) fetch_indices(src, m0 + 3 * kNT, islot[wave][3], wave, lane);
+    if (ntiles > 2) {
+      g2.decode(src, m0 + 2 * kNT, vmb + 8, wave, lane);
+      g2.all_rows(src, ring_off + 2 * kTileBytes, wave, lane);
+    }
+  };
+  prologue();
+  v8bf qf[2][kKs];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bool on = j ? sh1 : sh0;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + (on ? 16 * (2 * wave + j) + c : 0)) * kDQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks)
+      qf[j][ks] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
   }
-  vm_wait(0);  // Q and the first two tiles have landed
+  prologue_rest();
 
   // Softmax reference: m_ref is fixed at the first tile with a valid key and
   // never moved, so the accumulators are never rescaled.  Later scores may
@@ -217,117 +319,123 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   // numbers.  If a score goes beyond that headroom the block reruns its split
   // once with m_ref set to the true maximum seen in the first run.
   float m_ref[2] = {-INFINITY, -INFINITY}, m_seen[2] = {-INFINITY, -INFINITY}, l_part[2] = {0.f, 0.f};
-  v4f acc_o[kDbHalf][2];
+  v4f acc_o[kDbW][kMaxHB];
   const float qk_scale = a.sm_scale * kLog2e;
   bool overflow = false;
 
-  // The loops below are software-pipelined by hand: LDS reads run a few
-  // steps ahead of the MFMAs that consume them, and sched_barrier fences keep
-  // the scheduler from sinking them back next to their uses.
-  auto compute = [&](const unsigned char* tb, int q) {
-    // partial S^T[key, head] over this wave's share of the score dims; block
-    // kb row rho is key 16*kb + rho, so lane row g holds keys 4g..4g+3
-    // (kb = 0) and 16+4g..16+4g+3 (kb = 1).  Step n = 9*kb + i.
-    v4f sacc[2][2];
-    if (hb0) {
-      // rows 16*kb + c: key block 1 is 16 rows further down; (row & 7) is c & 7 for both
-      const unsigned char* arow = tb + aoff;
-      const unsigned char* rrow = tb + roff;
-      auto aload = [&](int n) -> v8bf {
-        const int kb = n / kKsHalf, i = n % kKsHalf;
-        const unsigned char* p = i < kKsMain ? arow + 16 * kMainRS * kb + 64 * i : rrow + 16 * kRopeRS * kb;
-        return as_v8bf(*reinterpret_cast<const v4i*>(p));
-      };
-      constexpr int kAhead = 3;
-      v8bf af[kAhead];
+  // Scores of one tile: S^T[key, head] over all 576 dims; block kb row rho
+  // is key 16*kb + rho, so lane row g holds keys 4g..4g+3 (kb = 0) and
+  // 16+4g..16+4g+3 (kb = 1).  Step n = kKs*kb + ks.  LDS reads run kAhead
+  // steps ahead of the MFMAs that consume them.
+  constexpr int kAhead = 4;
+  auto aload = [&](const unsigned char* tb, int n) -> v8bf {
+    const int kb = n / kKs, ks = n % kKs;
+    const unsigned char* p = ks < kKsMain ? tb + aoff + 16 * kMainRS * kb + 64 * ks
+                                          : tb + (ks == kKsMain ? roff0 : roff1) + 16 * kRopeRS * kb;
+    return as_v8bf(*reinterpret_cast<const v4i*>(p));
+  };
+  // hook(n) runs inside score step n (between fences), so other work can be
+  // spread over the MFMAs.
+  auto scores = [&](const unsigned char* tb, v4f (&sa)[2][2], auto&& hook) {
+    v8bf af[kAhead];
 #pragma unroll
-      for (int n = 0; n < kAhead; ++n) af[n] = aload(n);
+    for (int n = 0; n < kAhead; ++n) af[n] = aload(tb, n);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sacc[kb][0] = sacc[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 2; ++kb) sa[kb][0] = sa[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int n = 0; n < 2 * kKsHalf; ++n) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int kb = n / kKsHalf, i = n % kKsHalf;
-        sacc[kb][0] = mfma_bf16(af[n % kAhead], qf[0][i], sacc[kb][0]);
-        if (hb1) sacc[kb][1] = mfma_bf16(af[n % kAhead], qf[1][i], sacc[kb][1]);
-        if (n + kAhead < 2 * kKsHalf) af[n % kAhead] = aload(n + kAhead);
-      }
+    for (int n = 0; n < 2 * kKs; ++n) {
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xbuf[wave][j][lane] = sacc[j >> 1][j & 1];
+      const int kb = n / kKs, ks = n % kKs;
+      sa[kb][0] = mfma_bf16(af[n % kAhead], qf[0][ks], sa[kb][0]);
+      if (sh1) sa[kb][1] = mfma_bf16(af[n % kAhead], qf[1][ks], sa[kb][1]);
+      if (n + kAhead < 2 * kKs) af[n % kAhead] = aload(tb, n + kAhead);
+      hook(n);
     }
-    lds_barrier();  // both halves' partial scores are in LDS
-    if (!hb0) return;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[j >> 1][j & 1] += xbuf[wave ^ 4][j][lane];
-    // Scores of lane row g: sv[4*kb + i] is key 4g + 16*kb + i, whose
-    // validity bit is bit i of byte g + 4*kb of the slot's mask.  Masked keys
-    // become -inf through a bit select (km[j] is all ones for a valid key).
-    const uint64_t vm = vmask[q];
-    const uint32_t vl[2] = {(uint32_t)vm >> (8 * g), (uint32_t)(vm >> 32) >> (8 * g)};
-    uint32_t km[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) km[j] = (uint32_t)((int32_t)(vl[j >> 2] << (31 - (j & 3))) >> 31);
-    v8bf pf[2];
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float sv[8];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Softmax weights of one tile's scores (vm: its row-validity bits), rounded
+  // to bf16 and written to the P buffer, as kSoftSteps micro-steps so they
+  // can ride on the next tile's score MFMAs.  sv[4*kb + i] is key
+  // 16*kb + 4g + i; masked keys become -inf through a bit select.
+  constexpr int kSoftSteps = 19;
+  uint32_t vml;  // validity bits shifted so bit 16*kb + i is key 16*kb + 4g + i
+  float sv[8], tmax, nmr;
+  uint32_t pk[4];
+  auto soft_step = [&](int k, const v4f (&sa)[2][2], uint32_t vm) {
+    if (k == 0) {
+      vml = vm >> (4 * g);
+      return;
+    }
+    const int hb = (k - 1) / 9, st = (k - 1) % 9;
+    if (hb == 1 && !sh1) return;
+    if (st == 0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        sv[j] = __uint_as_float((km[j] & __float_as_uint(sacc[j >> 2][hb][j & 3])) | (~km[j] & 0xFF800000u));
-      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tmax = max_xor32(max_xor16(tmax)) * qk_scale;  // the scale is positive: max commutes with it
+        sv[j] = (vml >> (16 * (j >> 2) + (j & 3))) & 1u ? sa[j >> 2][hb][j & 3] : -INFINITY;
+    } else if (st == 1) {
+      tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    } else if (st == 2) {
+      tmax = max_xor16(tmax);
+    } else if (st == 3) {
+      tmax = max_xor32(tmax) * qk_scale;  // the scale is positive: max commutes with it
       m_seen[hb] = fmaxf(m_seen[hb], tmax);
       if (m_ref[hb] == -INFINITY) m_ref[hb] = tmax;  // nothing accumulated yet
       overflow = overflow || (tmax > m_ref[hb] + 64.f);
-      // p = 2^(s*scale - m_ref) rounded to bf16 (RNE, two per conversion); the
-      // normaliser sums the same rounded weights the PV product uses, so the
-      // output is an exact convex combination of value rows.  Without a
-      // reference yet every p is 0.  A score past the headroom may give inf
-      // here; that pass is discarded and rerun.
-      const float nmr = m_ref[hb] == -INFINITY ? -INFINITY : -m_ref[hb];
-      uint32_t pk[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * j], qk_scale, nmr));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * j + 1], qk_scale, nmr));
-        pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2bf));
-      }
+      // p = 2^(s*scale - m_ref) rounded to bf16 (RNE, two per conversion);
+      // the normaliser sums the same rounded weights the value product
+      // uses, so the output is an exact convex combination of value rows.
+      // Without a reference yet every p is 0.  A score past the headroom
+      // may give inf here; that pass is discarded and rerun.
+      nmr = m_ref[hb] == -INFINITY ? -INFINITY : -m_ref[hb];
+    } else if (st <= 7) {
+      const int j = st - 4;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[2 * j], qk_scale, nmr));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * j + 1], qk_scale, nmr));
+      pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2bf));
+    } else {
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) psum += __uint_as_float(pk[j] << 16) + __uint_as_float(pk[j] & 0xFFFF0000u);
       l_part[hb] += psum;
-      v4i pw = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-      pf[hb] = as_v8bf(pw);
+      *reinterpret_cast<v4i*>(pbuf + (16 * (2 * wave + hb)) * kPRow + poff) =
+          v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
     }
-    // O^T[dims, heads] += V^T[dims, keys] . P^T[keys, heads].  V^T fragments
-    // (16 dims x keys {4g..4g+3, 16+4g..16+4g+3} for lane row g) are two LDS
-    // transpose loads each: lane j of a 16-lane row supplies key kbase + j/4,
-    // dims 16db + 4*(j%4) .. +3.
+  };
+  // O^T[dims, heads] += V^T[dims, keys] . P^T[keys, heads].  V^T fragments
+  // (16 dims x keys {4g..4g+3, 16+4g..16+4g+3} for lane row g) are two LDS
+  // transpose loads each: lane j of a 16-lane row supplies key kbase + j/4,
+  // dims 16db + 4*(j%4) .. +3.
+  auto values = [&](const unsigned char* tb) {
+    v8bf pf[kMaxHB];
+#pragma unroll
+    for (int hb = 0; hb < kMaxHB; ++hb)
+      if (hb < NHB) pf[hb] = as_v8bf(*reinterpret_cast<const v4i*>(pbuf + 16 * hb * kPRow + poff));
     const unsigned char* v0 = tb + voff;
-    const unsigned char* v1 = v0 + 16 * kMainRS;
-    constexpr int kVAhead = 4;
+    auto vaddr = [&](int db) { return v0 + 32 * db; };  // rows + 16: 16 * kMainRS further
+    constexpr int kVAhead = 3;
     v4s vlo[kVAhead], vhi[kVAhead];
 #pragma unroll
     for (int db = 0; db < kVAhead; ++db) {
-      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v0 + 32 * db));
-      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v1 + 32 * db));
+      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(db));
+      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(db) + 16 * kMainRS));
     }
 #pragma unroll
-    for (int db = 0; db < kDbHalf; ++db) {
+    for (int db = 0; db < kDbW; ++db) {
       __builtin_amdgcn_sched_barrier(0);
       const int sl = db % kVAhead;
       const v8bf av =
           __builtin_bit_cast(v8bf, __builtin_shufflevector(vlo[sl], vhi[sl], 0, 1, 2, 3, 4, 5, 6, 7));
-      acc_o[db][0] = mfma_bf16(av, pf[0], acc_o[db][0]);
-      if (hb1) acc_o[db][1] = mfma_bf16(av, pf[1], acc_o[db][1]);
-      if (db + kVAhead < kDbHalf) {
-        vlo[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v0 + 32 * (db + kVAhead)));
-        vhi[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(v1 + 32 * (db + kVAhead)));
+#pragma unroll
+      for (int hb = 0; hb < kMaxHB; ++hb)
+        if (hb < NHB) acc_o[db][hb] = mfma_bf16(av, pf[hb], acc_o[db][hb]);
+      if (db + kVAhead < kDbW) {
+        vlo[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(db + kVAhead));
+        vhi[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(db + kVAhead) + 16 * kMainRS));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  static_assert(kSoftSteps + 1 <= 2 * kKs, "softmax micro-steps fit into the score steps");
 
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {  // rerun with the true maxima as references (no score can exceed them)
@@ -335,24 +443,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       m_ref[1] = m_seen[1];
       overflow = false;
       __syncthreads();
-      if (ntiles > 0) gather_tile(src, m0, ring, reinterpret_cast<unsigned char*>(&vmask[0]), wave, lane);
-      if (ntiles > 1) gather_tile(src, m0 + kNT, ring + kTileBytes, reinterpret_cast<unsigned char*>(&vmask[1]), wave, lane);
+      prologue();
+      prologue_rest();
     }
 #pragma unroll
-    for (int db = 0; db < kDbHalf; ++db) acc_o[db][0] = acc_o[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < kDbW; ++db)
+#pragma unroll
+      for (int hb = 0; hb < kMaxHB; ++hb) acc_o[db][hb] = v4f{0.f, 0.f, 0.f, 0.f};
     l_part[0] = l_part[1] = 0.f;
     if (tid == 0) overflow_flag = 0;
-    // Ring step: wait for this wave's share of tile tt, barrier (all shares
-    // landed; everyone is done with tile tt-1), refill the freed slot with
-    // tile tt+2, compute tile tt.  Every wave takes both barriers of a step.
-    int q = 0;  // ring slot of tile tt
+    if (ntiles == 0) break;
+    // Scores of tile 0 first: tile 0 and Q have landed once at most the
+    // copies issued after them (tile 1, idx(3), tile 2) are in flight.
+    vm_wait_n((ntiles > 1 ? kDma : 0) + (ntiles > 3 ? 1 : 0) + (ntiles > 2 ? kDma : 0));
+    lds_barrier();
+    v4f sacc[2][2];
+    if (sh0) scores(ring, sacc, [](int) {});
+    // Tile step tt: wait for tile tt+1 and the indices of tile tt+3, barrier
+    // (all shares landed; everyone is done with tile tt-1 and with the P
+    // buffer), copy burst (indices of tile tt+4, rows of tile tt+3 into the
+    // slot tile tt-1 used), scores of tile tt+1 interleaved with the softmax
+    // of tile tt, barrier (P complete), values of tile tt.  Per wave the
+    // copies go out in the order ..., idx(tt+3), rows(tt+2), idx(tt+4),
+    // rows(tt+3), so at most kDma copies in flight means rows(tt+1) and
+    // idx(tt+3) landed.
     for (int tt = 0; tt < ntiles; ++tt) {
-      vm_wait(tt + 1 < ntiles ? kDma : 0);
+      if (tt + 2 < ntiles)
+        vm_wait<kDma>();
+      else
+        vm_wait<0>();
       lds_barrier();
-      const int qn = q == 0 ? 2 : q - 1;  // slot of tile tt+2 (= slot of tile tt-1)
-      if (tt + 2 < ntiles) gather_tile(src, m0 + (tt + 2) * kNT, ring + qn * kTileBytes, reinterpret_cast<unsigned char*>(&vmask[qn]), wave, lane);
-      compute(ring + q * kTileBytes, q);
-      q = q == 2 ? 0 : q + 1;
+      if (tt + 4 < ntiles) fetch_indices(src, m0 + (tt + 4) * kNT, islot[wave][(tt + 4) & 3], wave, lane);
+      if (tt + 3 < ntiles) {
+        TileGather tg;
+        tg.read_lds(islot[wave][(tt + 3) & 3]);
+        tg.decode(src, m0 + (tt + 3) * kNT, vmb + 4 * ((tt + 3) & 3), wave, lane);
+        tg.all_rows(src, ring_off + ((tt + 3) & 3) * kTileBytes, wave, lane);
+      }
+      if (sh0) {
+        const uint32_t vm = vmask[tt & 3];
+        if (tt + 1 < ntiles) {
+          // softmax micro-step k rides on score step k + 1
+          v4f snext[2][2];
+          scores(ring + ((tt + 1) & 3) * kTileBytes, snext, [&](int n) {
+            if (n >= 1 && n <= kSoftSteps) soft_step(n - 1, sacc, vm);
+          });
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb][0] = snext[kb][0];
+            sacc[kb][1] = snext[kb][1];
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sacc, vm);
+        }
+      }
+      lds_barrier();  // P of every head is in LDS
+      values(ring + (tt & 3) * kTileBytes);
     }
     __syncthreads();
     if (overflow) overflow_flag = 1;
@@ -360,19 +507,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
     if (!overflow_flag) break;
   }
 
-  if (!hb0) return;
-  // Output through LDS (the ring is free now): each wave stages one 16-head
-  // block at a time as rows of 256 dims, then stores whole 512-byte half rows.
-  constexpr int kStageRS = 512 + 16;
-  unsigned char* stage = ring + wave * 16 * kStageRS;
+  // Normalisers: the wave that ran a head's softmax publishes 1/l (and the
+  // log-sum-exp or the split's (max, sum)).
   const Partials P = partials(a, ns);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    if (hb == 1 && !hb1) break;
-    const int head = h0 + 16 * hb + c;
+    if (!(hb ? sh1 : sh0)) break;
+    const int head = 16 * (2 * wave + hb) + c;
     const float l_tot = sum_xor32(sum_xor16(l_part[hb]));
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (g == 0 && half == 0) {
+    if (g == 0) {
+      hinv[head] = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (ns == 1) {
         if (a.lse) a.lse[(size_t)t * a.H + head] = l_tot > 0.f ? (m_ref[hb] + log2f(l_tot)) * kLn2 : -INFINITY;
       } else {
@@ -381,24 +525,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
         pml[1] = l_tot;
       }
     }
+  }
+  __syncthreads();
+  // Output through LDS (the ring is free now): each wave stages four 16-head
+  // blocks at a time as rows of its 128 dims, then stores whole 256-byte
+  // pieces of the output rows.
+  constexpr int kStageRS = 2 * (kDV / kWaves) + 16;
+  unsigned char* stage = ring + wave * 64 * kStageRS;
 #pragma unroll
-    for (int db = 0; db < kDbHalf; ++db) {
-      v2i st;
-      st[0] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][hb][0] * inv) |
-                    ((uint32_t)f32_to_bf16_rne(acc_o[db][hb][1] * inv) << 16));
-      st[1] = (int)((uint32_t)f32_to_bf16_rne(acc_o[db][hb][2] * inv) |
-                    ((uint32_t)f32_to_bf16_rne(acc_o[db][hb][3] * inv) << 16));
-      *reinterpret_cast<v2i*>(stage + c * kStageRS + 2 * (16 * db + 4 * g)) = st;
+  for (int half = 0; half < 2; ++half) {
+    if (64 * half >= 16 * NHB) break;
+#pragma unroll
+    for (int hl = 0; hl < 4; ++hl) {
+      const int hb = 4 * half + hl;
+      if (!(hb < NHB)) break;
+      const float inv = hinv[16 * hb + c];
+#pragma unroll
+      for (int db = 0; db < kDbW; ++db) {
+        // hardware round-to-nearest-even, two values per conversion
+        const v2bf lo = __builtin_convertvector((v2f){acc_o[db][hb][0] * inv, acc_o[db][hb][1] * inv}, v2bf);
+        const v2bf hi = __builtin_convertvector((v2f){acc_o[db][hb][2] * inv, acc_o[db][hb][3] * inv}, v2bf);
+        *reinterpret_cast<v2i*>(stage + (16 * hl + c) * kStageRS + 2 * (16 * db + 4 * g)) =
+            v2i{__builtin_bit_cast(int, lo), __builtin_bit_cast(int, hi)};
+      }
     }
     // the stage is private to this wave: its own LDS writes complete in order
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int hr = 2 * j + (lane >> 5);
-      const v4i v = *reinterpret_cast<const v4i*>(stage + hr * kStageRS + 16 * (lane & 31));
-      const int hh = h0 + 16 * hb + hr;
-      uint16_t* orow = ns == 1 ? static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hh) * kDV
-                               : P.o + (((size_t)r * ns + split) * a.H + hh) * kDV;
-      *reinterpret_cast<v4i*>(orow + 256 * half + 8 * (lane & 31)) = v;
+    for (int j = 0; j < 16; ++j) {
+      const int hr = 4 * j + (lane >> 4);
+      const int hh = 64 * half + hr;
+      if (hh < 16 * NHB) {
+        const v4i v = *reinterpret_cast<const v4i*>(stage + hr * kStageRS + 16 * (lane & 15));
+        uint16_t* orow = ns == 1 ? static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hh) * kDV
+                                 : P.o + (((size_t)r * ns + split) * a.H + hh) * kDV;
+        *reinterpret_cast<v4i*>(orow + (kDV / kWaves) * wave + 8 * (lane & 15)) = v;
+      }
     }
   }
 }
@@ -541,12 +702,18 @@ hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
   const int per = mla_per_split(a.k, ns);
   const int total = a.row_count * ns;
   const int per_xcd = (total + 7) / 8;
-  if (a.H % 32 == 0)
-    hipLaunchKernelGGL(k_mla_bf16<true>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns,
-                       per, per_xcd);
-  else
-    hipLaunchKernelGGL(k_mla_bf16<false>, dim3((unsigned)(8 * per_xcd)), dim3(kThreads), 0, stream, a, a.idx, ns,
-                       per, per_xcd);
+  const dim3 grid((unsigned)(8 * per_xcd)), block(kThreads);
+  switch (a.H / 16) {
+    case 1: hipLaunchKernelGGL(k_mla_bf16<1>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 2: hipLaunchKernelGGL(k_mla_bf16<2>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 3: hipLaunchKernelGGL(k_mla_bf16<3>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 4: hipLaunchKernelGGL(k_mla_bf16<4>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 5: hipLaunchKernelGGL(k_mla_bf16<5>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 6: hipLaunchKernelGGL(k_mla_bf16<6>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 7: hipLaunchKernelGGL(k_mla_bf16<7>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    case 8: hipLaunchKernelGGL(k_mla_bf16<8>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+    default: return hipErrorInvalidValue;
+  }
   if (ns > 1)
     hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(a.row_count * (a.H / 16))), dim3(256), 0, stream, a, ns);
   return hipGetLastError();
