@@ -566,65 +566,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
 
 // Merge split partials: each split stored its output normalised by its own
 // sum l_s together with (m_s, l_s); out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s.
-// A block covers one row and 16 heads; 16 threads per head, 32 dims each.
-// All of a thread's partial loads are issued before any is used.
+// A wave merges one (row, head): lane l holds dims 8l..8l+7, so each split's
+// partial row is one contiguous 1 KB load (all issued before any is used).
+// Blocks for a row run on the XCD that ran its first split (the split
+// kernel gives XCD x the flat (row, split) indices [x*per_xcd,
+// (x+1)*per_xcd)), whose L2 saw the partials written.
 constexpr int kCombineMaxSplits = 8;
-__global__ __launch_bounds__(256) void k_mla_combine(MlaArgs a, int ns) {
-  const int hg = a.H / 16;
-  const int r = (int)blockIdx.x / hg;
-  const int h = ((int)blockIdx.x % hg) * 16 + (int)threadIdx.x / 16;
-  const int d = 32 * ((int)threadIdx.x % 16);
+constexpr int kCombineHeads = 4;  // heads (waves) per block
+__global__ __launch_bounds__(64 * kCombineHeads) void k_mla_combine(MlaArgs a, int ns, int per_xcd) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+  const int hpb = a.H / kCombineHeads;  // blocks per row
+  const int r0 = (x * per_xcd + ns - 1) / ns;
+  const int r1 = min(a.row_count, ((x + 1) * per_xcd + ns - 1) / ns);
+  const int r = r0 + j / hpb;
+  if (r >= r1) return;
+  const int h = (j % hpb) * kCombineHeads + wave;
   const int t = a.row_begin + r;
   const Partials P = partials(a, ns);
   float ms[kCombineMaxSplits], ls[kCombineMaxSplits];
-  v4i o[kCombineMaxSplits][4];
+  v4i o[kCombineMaxSplits];
 #pragma unroll
-  for (int s = 0; s < kCombineMaxSplits; ++s) {
-    if (s < ns) {
-      const float* ml = P.ml + (((size_t)r * ns + s) * a.H + h) * 2;
-      ms[s] = ml[0];
-      ls[s] = ml[1];
-      const v4i* src = reinterpret_cast<const v4i*>(P.o + (((size_t)r * ns + s) * a.H + h) * kDV + d);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[s][i] = src[i];
+  for (int sp = 0; sp < kCombineMaxSplits; ++sp) {
+    if (sp < ns) {
+      const size_t rs = ((size_t)r * ns + sp) * a.H + h;
+      ms[sp] = P.ml[rs * 2];
+      ls[sp] = P.ml[rs * 2 + 1];
+      o[sp] = *reinterpret_cast<const v4i*>(P.o + rs * kDV + 8 * lane);
     }
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kCombineMaxSplits; ++s)
-    if (s < ns) M = fmaxf(M, ms[s]);
+  for (int sp = 0; sp < kCombineMaxSplits; ++sp)
+    if (sp < ns) M = fmaxf(M, ms[sp]);
   float wsum = 0.f;
-  float acc[32];
+  float acc[8];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) acc[e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int s = 0; s < kCombineMaxSplits; ++s) {
-    if (s < ns && ms[s] != -INFINITY) {
-      const float wgt = exp2f(ms[s] - M) * ls[s];
+  for (int sp = 0; sp < kCombineMaxSplits; ++sp) {
+    if (sp < ns && ms[sp] != -INFINITY) {
+      const float wgt = exp2f(ms[sp] - M) * ls[sp];
       wsum += wgt;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t u = (uint32_t)o[s][i][j];
-          acc[8 * i + 2 * j] += wgt * __uint_as_float(u << 16);
-          acc[8 * i + 2 * j + 1] += wgt * __uint_as_float(u & 0xFFFF0000u);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t u = (uint32_t)o[sp][e];
+        acc[2 * e] += wgt * __uint_as_float(u << 16);
+        acc[2 * e + 1] += wgt * __uint_as_float(u & 0xFFFF0000u);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  v4i* orow = reinterpret_cast<v4i*>(static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + h) * kDV + d);
+  v4i st;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v4i st;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      st[j] = (int)((uint32_t)f32_to_bf16_rne(acc[8 * i + 2 * j] * inv) |
-                    ((uint32_t)f32_to_bf16_rne(acc[8 * i + 2 * j + 1] * inv) << 16));
-    orow[i] = st;
-  }
-  if (a.lse && (threadIdx.x % 16) == 0)
-    a.lse[(size_t)t * a.H + h] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
+  for (int e = 0; e < 4; ++e)
+    st[e] = __builtin_bit_cast(int, __builtin_convertvector((v2f){acc[2 * e] * inv, acc[2 * e + 1] * inv}, v2bf));
+  *reinterpret_cast<v4i*>(static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + h) * kDV + 8 * lane) = st;
+  if (a.lse && lane == 0) a.lse[(size_t)t * a.H + h] = wsum > 0.f ? (M + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 // fp32 path: one block per (row, head); scores of the selected rows in LDS.
@@ -714,8 +713,11 @@ hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
     case 8: hipLaunchKernelGGL(k_mla_bf16<8>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
     default: return hipErrorInvalidValue;
   }
-  if (ns > 1)
-    hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(a.row_count * (a.H / 16))), dim3(256), 0, stream, a, ns);
+  if (ns > 1) {
+    // per XCD at most ceil(per_xcd / ns) + 1 rows have their first split there
+    const int cpx = ((per_xcd + ns - 1) / ns + 1) * (a.H / kCombineHeads);
+    hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(8 * cpx)), dim3(64 * kCombineHeads), 0, stream, a, ns, per_xcd);
+  }
   return hipGetLastError();
 }
 
