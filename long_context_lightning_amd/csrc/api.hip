@@ -65,8 +65,6 @@ IndexerArgs make_indexer_args(const dsa_geom* g, const void* q, const float* q_s
   a.row_count = 0;
   a.scores = nullptr;
   a.ld = 0;
-  a.hist = nullptr;
-  a.hist_stride = 0;
   return a;
 }
 
@@ -78,7 +76,6 @@ hipError_t run_indexer(const IndexerArgs& a, bool fp8, hipStream_t stream) {
     c.row_begin = r0;
     c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
     c.scores = a.scores + (long long)(r0 - a.row_begin) * a.ld;
-    if (a.hist) c.hist = a.hist + (long long)(r0 - a.row_begin) * a.hist_stride;
     const hipError_t e = fp8 ? launch_indexer_fp8(c, stream) : launch_indexer_f32(c, stream);
     if (e != hipSuccess) return e;
   }
@@ -226,7 +223,6 @@ dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld, int32
   a.k = k;
   a.idx = idx;
   a.ws = ws;
-  a.hist_ready = 0;
   return hip_status(run_topk(a, stream));
 }
 
@@ -291,16 +287,10 @@ dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_s
       ta.k = topk;
       ta.idx = idx_out + (long long)r0 * topk;
       ta.ws = wsb + p.topk_off;
-      // fp8 scores: the indexer epilogue accumulates the threshold histogram
-      ta.hist_ready = fp8 ? 1 : 0;
-      if (fp8) e = launch_topk_zero(ta, stream);
-      if (e != hipSuccess) break;
       ia.row_begin = r0;
       ia.row_count = rc;
       ia.scores = scores;
       ia.ld = geom->S_max;
-      ia.hist = fp8 ? static_cast<uint32_t*>(ta.ws) : nullptr;
-      ia.hist_stride = topk_hist_stride_words(topk);
       e = run_indexer(ia, fp8, stream);
       if (e != hipSuccess) break;
       e = run_topk(ta, stream);

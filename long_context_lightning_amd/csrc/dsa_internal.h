@@ -178,14 +178,7 @@ struct IndexerArgs {
   int row_begin, row_count;
   float* scores;          // [row_count, ld]
   long long ld;
-  uint32_t* hist;         // optional: per-row histogram of the scores' top 12 order-key bits
-  long long hist_stride;  // words between consecutive rows' histograms
 };
-
-// Histogram bins of the top-k threshold search: the top 12 bits of a score's
-// order key (sign, exponent, 3 mantissa bits).
-constexpr int kHistBins = 4096;
-constexpr int kHistShift = 20;
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t s);
 hipError_t launch_indexer_f32(const IndexerArgs& a, hipStream_t s);
@@ -198,12 +191,9 @@ struct TopkArgs {
   int row_begin, row_count, k;
   int32_t* idx;           // [row_count, k]
   void* ws;
-  int hist_ready;         // 1: the row histograms were already accumulated (by the indexer)
 };
 
 size_t topk_workspace_bytes(int row_count, int S_max, int k);
-long long topk_hist_stride_words(int k);   // per-row stride of the histograms in the workspace
-hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 struct MlaArgs {

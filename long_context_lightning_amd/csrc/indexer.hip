@@ -56,9 +56,8 @@ __device__ __forceinline__ RowGroup row_group(const IndexerArgs& a) {
   return RowGroup{b, t0, t1 - t0};
 }
 
-template <int NQ, bool WBF16, bool HIST>
+template <int NQ, bool WBF16>
 __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
-  __shared__ uint32_t lhist[HIST ? NQ * kHistBins : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -83,10 +82,6 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
     for (int r = 0; r < rg.nr; ++r) out[(long long)r * a.ld + s] = -INFINITY;
   if (kend <= chunk0) return;
   const int nsteps = (kend - chunk0 + kKeysPerBlock - 1) / kKeysPerBlock;
-  if (HIST) {
-    for (int i = threadIdx.x; i < NQ * kHistBins; i += 256) lhist[i] = 0u;
-    __syncthreads();
-  }
 
   const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
   const float* ksb = a.k_scale ? a.k_scale + (size_t)rg.b * a.S_max : nullptr;
@@ -158,23 +153,12 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
       if (r < rg.nr && s_l < kend) {
         const float v = tot * ks_cur;
         out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? v : -INFINITY;
-        if (HIST && s_l <= pos[r]) atomicAdd(&lhist[r * kHistBins + (order_key(v) >> kHistShift)], 1u);
       }
     }
     if (step + 1 < nsteps) {
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) kf_cur[blk] = kf_nxt[blk];
       ks_cur = ks_nxt;
-    }
-  }
-  if (HIST) {
-    // flush the block's histogram: one global atomic per non-empty bin
-    __syncthreads();
-    for (int i = threadIdx.x; i < NQ * kHistBins; i += 256) {
-      const int r = i / kHistBins;
-      const uint32_t v = lhist[i];
-      if (v && r < rg.nr)
-        atomicAdd(&a.hist[(long long)(rg.t0 + r - a.row_begin) * a.hist_stride + (i - r * kHistBins)], v);
     }
   }
 }
@@ -230,10 +214,7 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
 
 template <int NQ, bool WBF16>
 static void launch_fp8_variant(const IndexerArgs& a, dim3 grid, hipStream_t stream) {
-  if (a.hist)
-    hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, false>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16>), grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t stream) {

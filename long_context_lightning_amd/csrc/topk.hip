@@ -8,13 +8,11 @@
 //  1. zero   -- clear the per-row histograms and counters in the workspace.
 //  2. hist   -- (row, 8192-score segment) blocks: LDS histogram of the top 12
 //               bits of each score's order key, flushed with global atomics.
-//               (dsa_forward skips 1-2 here: it zeroes before the indexer,
-//               whose epilogue accumulates the same histogram.)
 //  3. gather -- same blocks: every block finds the threshold bin b* (the bin
 //               holding the k-th largest) from the row histogram and appends
 //               the (key, position) of every score in bins >= b* to the row's
 //               candidate list, reserving its range with one atomic.
-//  4. final  -- one 256-thread block per row: exact radix select (8-bit
+//  4. final  -- one 1024-thread block per row: exact radix select (8-bit
 //               digits) of the k-th key tau inside bin b*; positions with
 //               key > tau and the copies of tau go into two LDS bitmaps; the
 //               lower-position tie rule keeps the copies up to the want-th
@@ -28,11 +26,11 @@ namespace dsa {
 
 namespace {
 
-constexpr int kBins = kHistBins;       // top 12 bits of the order key
-constexpr int kBinShift = kHistShift;
+constexpr int kBins = 4096;     // histogram bins: top 12 bits of the order key (sign, exponent, 3 mantissa bits)
+constexpr int kBinShift = 20;
 constexpr int kSeg = 8192;      // scores per hist/gather block
 constexpr int kSegThreads = 256;
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 1024;
 constexpr int kDigitBits = 8;   // radix digit width of the exact selection
 constexpr int kMaxK = 4096;
 constexpr int kMaxS = 262144;
@@ -283,13 +281,6 @@ size_t final_lds_bytes(int S_max, int k) {
 
 }  // namespace
 
-long long topk_hist_stride_words(int k) { return (long long)(row_stride_bytes(k) / 4); }
-
-hipError_t launch_topk_zero(const TopkArgs& a, hipStream_t stream) {
-  if (a.row_count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
 
 size_t topk_workspace_bytes(int row_count, int S_max, int k) {
   (void)S_max;
@@ -304,10 +295,8 @@ bool topk_supported(int S_max, int k) {
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
   const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);
-  if (!a.hist_ready) {
-    hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
-  }
+  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
   hipLaunchKernelGGL(k_topk_gather, segs, dim3(kSegThreads), 0, stream, a);
   const size_t lds = final_lds_bytes(a.S_max, a.k);
   hipLaunchKernelGGL(k_topk_final, dim3((unsigned)a.row_count), dim3(kFinThreads), lds, stream, a);
