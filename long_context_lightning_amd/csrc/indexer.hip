@@ -2,7 +2,7 @@
 //
 //   I[t,s] = k_scale[s] * sum_j w[t,j]*q_scale[t,j] * ReLU(q[t,j,:] . k[s,:])
 //
-// fp8 path: a block owns a 2048-key chunk of one sequence and up to NQ query
+// fp8 path: a block owns a 4096-key chunk of one sequence and up to NQ query
 // rows of that sequence; its four waves step through the chunk 64 keys each
 // per step, with the next step's key fragments loaded while the current step
 // computes.  The 64x128 query tile of a row stays in
@@ -24,7 +24,7 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 constexpr int kKeysPerWave = 64;                               // keys per wave per step
 constexpr int kKeysPerBlock = kWavesPerBlock * kKeysPerWave;   // keys per block per step
-constexpr int kKeysPerChunk = 2048;                            // keys streamed by one block
+constexpr int kKeysPerChunk = 4096;                            // keys streamed by one block
 
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   v4i lo = *reinterpret_cast<const v4i*>(p);
@@ -89,11 +89,11 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
     const int kw = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave;
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const int s = kw + 16 * blk + c;
-      kf[blk] = (s < kend) ? load32(kb + (size_t)s * kDI + 32 * g) : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+      const int s = min(kw + 16 * blk + c, kend - 1);  // keys past kend are never stored
+      kf[blk] = load32(kb + (size_t)s * kDI + 32 * g);
     }
-    const int s_l = kw + lane;
-    ks = (ksb && s_l < kend) ? ksb[s_l] : 1.0f;
+    const int s_l = min(kw + lane, kend - 1);
+    ks = ksb ? ksb[s_l] : 1.0f;
   };
   v8i kf_cur[4], kf_nxt[4];
   float ks_cur, ks_nxt;
