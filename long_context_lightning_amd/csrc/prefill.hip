@@ -311,6 +311,145 @@ __device__ uint32_t wave_trim(uint32_t* ekey, uint32_t* eidx, int& n, int want, 
   return tau;
 }
 
+// Exact compaction with the keys staged in LDS (lk: this wave's kLdsList
+// words): the keys come in with one copy, the min/max and every radix pass
+// read LDS, and the positions are read once, on the way out.  Same result
+// as wave_compact.  A radix pass whose selected bin is taken whole ends the
+// search: every key at or above the bin's floor is kept and tau is that
+// floor (no dropped key reaches it, so later keys equal to it still lose).
+// FINAL: the kept positions go to pout[0..want), -1 padded, instead of back
+// into the list (a list of at most `want` entries is copied out as it is).
+constexpr int kLdsList = 4096;
+template <bool FINAL>
+__device__ uint32_t wave_compact_lds(uint32_t* ekey, uint32_t* eidx, int& n, int want, int cap, uint32_t* hist,
+                                     uint32_t* lk, int32_t* pout) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  const int nn = n;
+  if (!FINAL && nn <= want) return 0u;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's candidate stores have landed
+  wave_sync_mem();
+  const bool select = nn > want;
+  uint32_t tau = 0u, rem = (uint32_t)want;
+  if (select) {
+    // Lane l copies words 256b + 4l .. 256b + 4l + 3 of 1 KB block b.
+    const int nblk = (nn + 255) / 256;
+    for (int b = 0; b < nblk; ++b)
+      dma16_lds(ekey, 4u * (uint32_t)min(256 * b + 4 * lane, cap - 4), lk + 256 * b);
+    __builtin_amdgcn_s_waitcnt(0);
+    wave_sync_mem();
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int i = 4 * lane; i < nn; i += 256) {
+      const v4i v = *reinterpret_cast<const v4i*>(lk + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (i + e < nn) {
+          mn = min(mn, (uint32_t)v[e]);
+          mx = max(mx, (uint32_t)v[e]);
+        }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    tau = mn;
+    if (mn != mx) {
+      const int common = __clz(mn ^ mx);  // leading bits shared by every key
+      int rem_bits = 32 - common;
+      uint32_t prefix = common == 0 ? 0u : (mn & (0xFFFFFFFFu << rem_bits));
+      while (rem_bits > 0) {
+        const int nb = rem_bits < 8 ? rem_bits : 8;
+        const int shift = rem_bits - nb;
+        const uint32_t dmask = (1u << nb) - 1u;
+        for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+        wave_sync_mem();
+        const uint32_t hi = rem_bits >= 32 ? 0u : prefix >> rem_bits;
+        for (int i = 4 * lane; i < nn; i += 256) {
+          const v4i v = *reinterpret_cast<const v4i*>(lk + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t u = (uint32_t)v[e];
+            if (i + e < nn && (rem_bits >= 32 ? 0u : u >> rem_bits) == hi) atomicAdd(&hist[(u >> shift) & dmask], 1u);
+          }
+        }
+        wave_sync_mem();
+        const int d0 = 4 * (63 - lane);
+        uint32_t c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[j] = hist[d0 + 3 - j];
+          tot += c[j];
+        }
+        const uint32_t above = wave_inclusive_sum(tot) - tot;
+        uint32_t dsel = 0, asel = 0, csel = 0;
+        const bool mine = above < rem && rem <= above + tot;
+        if (mine) {
+          uint32_t acc = above;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (acc < rem && rem <= acc + c[j]) {
+              dsel = (uint32_t)(d0 + 3 - j);
+              asel = acc;
+              csel = c[j];
+            }
+            acc += c[j];
+          }
+        }
+        const unsigned long long who = __ballot(mine);
+        const int src = __ffsll((long long)who) - 1;
+        dsel = (uint32_t)__shfl((int)dsel, src, 64);
+        asel = (uint32_t)__shfl((int)asel, src, 64);
+        csel = (uint32_t)__shfl((int)csel, src, 64);
+        prefix |= dsel << shift;
+        rem -= asel;
+        rem_bits = shift;
+        wave_sync_mem();
+        if (csel == rem) break;  // the whole bin is kept
+      }
+      tau = prefix;
+    }
+  }
+  // Keep key > tau and the first `rem` copies of tau, in list order, 64
+  // entries a step (entry 64j + lane).  Kept entries only move down (slot <=
+  // index) and a batch's positions are read before its writes: in place.
+  int w = 0;
+  uint32_t eq_seen = 0;
+  const int nstr = (nn + 63) / 64;
+  constexpr int kWB = 16;
+  for (int j0 = 0; j0 < nstr; j0 += kWB) {
+    uint32_t p[kWB];
+#pragma unroll
+    for (int jj = 0; jj < kWB; ++jj) p[jj] = eidx[min(64 * (j0 + jj) + lane, nn - 1)];
+    wave_sync_mem();
+#pragma unroll
+    for (int jj = 0; jj < kWB; ++jj) {
+      if (j0 + jj < nstr) {
+        const int i = 64 * (j0 + jj) + lane;
+        const uint32_t u = lk[min(i, kLdsList - 1)];
+        const bool eq = select && i < nn && u == tau;
+        const unsigned long long eqb = __ballot(eq);
+        const uint32_t eq_rank = eq_seen + (uint32_t)__popcll(eqb & lt);
+        const bool keep = i < nn && (!select || u > tau || (eq && eq_rank < rem));
+        const unsigned long long kb = __ballot(keep);
+        if (keep) {
+          const int slot = w + __popcll(kb & lt);
+          if (FINAL) {
+            pout[slot] = (int32_t)p[jj];
+          } else {
+            ekey[slot] = u;
+            eidx[slot] = p[jj];
+          }
+        }
+        w += __popcll(kb);
+        eq_seen += (uint32_t)__popcll(eqb);
+      }
+    }
+  }
+  if (FINAL)
+    for (int j = w + lane; j < want; j += 64) pout[j] = -1;
+  n = w;
+  wave_sync_mem();
+  return tau;
+}
+
 __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
   constexpr int R = kRowsPerWave;
   // K tiles: 128-byte rows, the 16-byte chunk ch of key j at slot ch ^ (j & 7)
@@ -318,6 +457,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kNK * kDI];
   __shared__ float ksc[2][kNK];
   __shared__ uint32_t hist[kWaves][256];  // per-wave compaction histograms
+  __shared__ __attribute__((aligned(16))) uint32_t lkeys[kWaves][kLdsList];  // per-wave staged list keys
   __shared__ int need_compact;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -506,8 +646,13 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
 #pragma unroll
       for (int rr = 0; rr < R; ++rr)
         if (n[rr] > trigger) {
-          uint32_t tau = wave_trim(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
-          if (n[rr] > trigger) tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+          uint32_t tau;
+          if (cap <= kLdsList) {
+            tau = wave_compact_lds<false>(ekey[rr], eidx[rr], n[rr], k, cap, hist[wave], lkeys[wave], nullptr);
+          } else {
+            tau = wave_trim(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+            if (n[rr] > trigger) tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+          }
           theta[rr] = max(theta[rr], tau);
         }
       __syncthreads();
@@ -530,8 +675,12 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
       for (int j = lane; j < k; j += 64) out[j] = (j <= rpos[rr]) ? j : -1;
       continue;
     }
-    wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
-    for (int j = lane; j < k; j += 64) out[j] = (j < n[rr]) ? (int32_t)eidx[rr][j] : -1;
+    if (cap <= kLdsList) {
+      wave_compact_lds<true>(ekey[rr], eidx[rr], n[rr], k, cap, hist[wave], lkeys[wave], out);
+    } else {
+      wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+      for (int j = lane; j < k; j += 64) out[j] = (j < n[rr]) ? (int32_t)eidx[rr][j] : -1;
+    }
   }
 }
 
