@@ -65,6 +65,10 @@ IndexerArgs make_indexer_args(const dsa_geom* g, const void* q, const float* q_s
   a.row_count = 0;
   a.scores = nullptr;
   a.ld = 0;
+  a.zero_base = nullptr;
+  a.zero_stride = 0;
+  a.zero_words = 0;
+  a.zero_rows = 0;
   return a;
 }
 
@@ -91,6 +95,7 @@ hipError_t run_topk(const TopkArgs& a, hipStream_t stream) {
     c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
     c.scores = a.scores + (long long)(r0 - a.row_begin) * a.ld;
     c.idx = a.idx + (long long)(r0 - a.row_begin) * a.k;
+    c.ws_zeroed = r0 == a.row_begin ? a.ws_zeroed : 0;  // later chunks reuse the workspace
     const hipError_t e = launch_topk(c, stream);
     if (e != hipSuccess) return e;
   }
@@ -223,6 +228,7 @@ dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld, int32
   a.k = k;
   a.idx = idx;
   a.ws = ws;
+  a.ws_zeroed = 0;
   return hip_status(run_topk(a, stream));
 }
 
@@ -287,10 +293,13 @@ dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_s
       ta.k = topk;
       ta.idx = idx_out + (long long)r0 * topk;
       ta.ws = wsb + p.topk_off;
+      ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
       ia.row_begin = r0;
       ia.row_count = rc;
       ia.scores = scores;
       ia.ld = geom->S_max;
+      topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
+      ia.zero_rows = rc;
       e = run_indexer(ia, fp8, stream);
       if (e != hipSuccess) break;
       e = run_topk(ta, stream);

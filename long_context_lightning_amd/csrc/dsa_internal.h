@@ -178,6 +178,12 @@ struct IndexerArgs {
   int row_begin, row_count;
   float* scores;          // [row_count, ld]
   long long ld;
+  // Optional side job: zero zero_words words at zero_base + r * zero_stride
+  // for r < zero_rows (the top-k counters of the same rows), so the top-k
+  // that follows needs no clearing launch of its own.
+  uint32_t* zero_base;
+  long long zero_stride;
+  int zero_words, zero_rows;
 };
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t s);
@@ -191,9 +197,12 @@ struct TopkArgs {
   int row_begin, row_count, k;
   int32_t* idx;           // [row_count, k]
   void* ws;
+  int ws_zeroed;          // the counters in ws are already zero (cleared by the indexer launch)
 };
 
 size_t topk_workspace_bytes(int row_count, int S_max, int k);
+// The words of a top-k workspace that must be zero before launch_topk.
+void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* stride_words, int* words);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 
 struct MlaArgs {

@@ -56,8 +56,20 @@ __device__ __forceinline__ RowGroup row_group(const IndexerArgs& a) {
   return RowGroup{b, t0, t1 - t0};
 }
 
+// The zeroing side job (see IndexerArgs), spread over every block of the launch.
+__device__ __forceinline__ void zero_side_job(const IndexerArgs& a) {
+  if (!a.zero_base) return;
+  const int nthreads = (int)(gridDim.x * gridDim.y * blockDim.x);
+  const int total = a.zero_rows * a.zero_words;
+  for (int i = (int)((blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x); i < total; i += nthreads) {
+    const int r = i / a.zero_words, j = i - r * a.zero_words;
+    a.zero_base[(long long)r * a.zero_stride + j] = 0u;
+  }
+}
+
 template <int NQ, bool WBF16>
 __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
+  zero_side_job(a);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -168,6 +180,7 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
 __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
   __shared__ float qs[kHI * kDI];
   __shared__ float wsh[kHI];
+  zero_side_job(a);
   const int t = a.row_begin + (int)blockIdx.y;
   const int b = t / a.q_len;
   const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);

@@ -292,10 +292,16 @@ bool topk_supported(int S_max, int k) {
   return k >= 1 && k <= kMaxK && S_max >= 1 && S_max <= kMaxS && final_lds_bytes(S_max, k) <= 160 * 1024;
 }
 
+void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* stride_words, int* words) {
+  *base = static_cast<uint32_t*>(ws);
+  *stride_words = (long long)(row_stride_bytes(k) / 4);
+  *words = rows > 0 ? kBins + 64 : 0;  // hist and meta are contiguous
+}
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
   const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);
-  hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
+  if (!a.ws_zeroed) hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);
   hipLaunchKernelGGL(k_topk_gather, segs, dim3(kSegThreads), 0, stream, a);
   const size_t lds = final_lds_bytes(a.S_max, a.k);
