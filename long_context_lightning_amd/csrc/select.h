@@ -154,4 +154,38 @@ __device__ uint32_t bitmap_select_emit(uint32_t* bitmap, const uint32_t* tbits, 
   return total;
 }
 
+// Writes the set positions of `bitmap` (n positions, zero up to the next
+// multiple of 4 words) in ascending order to out[0..limit).  Thread t owns
+// the contiguous 16-byte groups [t*per, (t+1)*per).  Returns the number of
+// set positions.  `sm` needs NT/64 + 4 words.  Block-wide.
+template <int NT>
+__device__ uint32_t bitmap_emit(const uint32_t* bitmap, int n, int32_t* out, uint32_t limit, uint32_t* sm) {
+  const int W4 = (((n + 31) >> 5) + 3) >> 2;  // 16-byte groups
+  const int per4 = (W4 + NT - 1) / NT;
+  const int g0 = (int)threadIdx.x * per4, g1 = min(g0 + per4, W4);
+  const v4i* b4 = reinterpret_cast<const v4i*>(bitmap);
+  uint32_t cnt = 0;
+  for (int gi = g0; gi < g1; ++gi) {
+    const v4i b = b4[gi];
+    cnt += __popc((uint32_t)b[0]) + __popc((uint32_t)b[1]) + __popc((uint32_t)b[2]) + __popc((uint32_t)b[3]);
+  }
+  uint32_t total;
+  uint32_t off = block_exclusive_sum<NT>(cnt, sm, &total);
+  for (int gi = g0; gi < g1; ++gi) {
+    const v4i b = b4[gi];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t bits = (uint32_t)b[j];
+      while (bits) {
+        const int bb = __ffs(bits) - 1;
+        if (off < limit) out[off] = 32 * (4 * gi + j) + bb;
+        ++off;
+        bits &= bits - 1u;
+      }
+    }
+  }
+  return total;
+}
+
 }  // namespace dsa
+

@@ -31,11 +31,13 @@ constexpr int kBinShift = 20;
 constexpr int kSeg = 8192;      // scores per hist/gather block
 constexpr int kSegThreads = 256;
 constexpr int kFinThreads = 1024;
-constexpr int kDigitBits = 8;   // radix digit width of the exact selection
+constexpr int kDigitBits = 8;   // radix digit width of the selection from a score row
+constexpr int kFinDigit = 10;   // radix digit width of the selection inside bin b*
 constexpr int kMaxK = 4096;
 constexpr int kMaxS = 262144;
 
 __host__ __device__ inline size_t cap_for(int k) { return (size_t)2 * k + 4096; }
+constexpr int kCapMax = 2 * kMaxK + 4096;  // candidate list bound (k = kMaxK)
 __host__ __device__ inline size_t row_stride_bytes(int k) {
   size_t b = (size_t)kBins * 4 + 256 + cap_for(k) * 8;
   return (b + 255) & ~(size_t)255;
@@ -186,13 +188,14 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
 __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   constexpr int NW = kFinThreads / 64;
-  uint32_t* whist = dyn;                          // NW << kDigitBits
-  uint32_t* sm = whist + (NW << kDigitBits);      // 64
+  constexpr int kCPer = kCapMax / kFinThreads;        // candidates per thread at most
+  static_assert(kFinThreads == 1 << kFinDigit, "one digit bin per thread");
   const int Wmax = (((a.S_max + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
-  uint32_t* bitmap = sm + 64;            // positions with key > tau (16-byte aligned)
-  uint32_t* tbits = bitmap + Wmax;       // positions with key == tau
-  uint32_t* skey = tbits + Wmax;         // cap
-  uint32_t* sidx = skey + cap_for(a.k);  // cap
+  uint32_t* bitmap = dyn;                              // positions kept (16-byte aligned)
+  uint32_t* tbits = bitmap + Wmax;                     // copies of tau, when ties need the position rule
+  uint32_t* hist = tbits + Wmax;                       // 1 << kFinDigit (16-byte aligned)
+  uint32_t* whist = hist + (1 << kFinDigit);           // NW << kDigitBits (score-row path)
+  uint32_t* sm = whist + (NW << kDigitBits);           // 64
 
   const int r = blockIdx.x;
   const int n = row_valid_count(a, r);
@@ -203,71 +206,123 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
     return;
   }
   RowWs w = row_ws(a.ws, r, a.k);
+  // The candidate list goes to registers first (its length is the gather
+  // launch's count), so the loads overlap the threshold search.
+  const uint32_t cap = (uint32_t)cap_for(a.k);
+  const uint32_t cnt = min(w.meta[0], cap);
+  uint32_t ck[kCPer], cp[kCPer];
+#pragma unroll
+  for (int j = 0; j < kCPer; ++j) {
+    const uint32_t i = (uint32_t)(tid + j * kFinThreads);
+    const uint32_t ic = i < cnt ? i : (cnt ? cnt - 1 : 0u);
+    ck[j] = w.ekey[ic];
+    cp[j] = w.eidx[ic];
+  }
   uint32_t bstar, above;
   find_threshold_bin<kFinThreads>(w.hist, (uint32_t)a.k, sm, &bstar, &above);
   const uint32_t total = above + w.hist[bstar];
-  const bool direct = total > cap_for(a.k);
+  const bool direct = total > cap;
   const float* row = a.scores + (long long)r * a.ld;
+  const int W4 = (((n + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
 
-  uint32_t tau, want;
   if (!direct) {
-    // candidates to LDS, eight loads in flight per thread
-    constexpr int kU = 8;
-    for (uint32_t i0 = 0; i0 < total; i0 += kU * kFinThreads) {
-      uint32_t kk[kU], ii[kU];
+    // Entries with bin > b* are all taken; the rest is resolved inside bin
+    // b* with kFinDigit-bit digits, one histogram bin per thread.  A digit
+    // bin that is taken whole ends the search: every key at or above its
+    // floor is kept (the common case, ties being rare).
+    uint32_t prefix = bstar << kBinShift, want = (uint32_t)a.k - above;
+    int rem_bits = kBinShift;
+    bool whole = false;
+    while (rem_bits > 0) {
+      const int nb = rem_bits < kFinDigit ? rem_bits : kFinDigit;
+      const int shift = rem_bits - nb;
+      const uint32_t dmask = (1u << nb) - 1u;
+      hist[tid] = 0u;
+      __syncthreads();
+      const uint32_t hi = prefix >> rem_bits;
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const uint32_t i = i0 + j * kFinThreads + tid;
-        kk[j] = i < total ? w.ekey[i] : 0u;
-        ii[j] = i < total ? w.eidx[i] : 0u;
-      }
+      for (int j = 0; j < kCPer; ++j)
+        if ((uint32_t)(tid + j * kFinThreads) < total && (ck[j] >> rem_bits) == hi)
+          atomicAdd(&hist[(ck[j] >> shift) & dmask], 1u);
+      __syncthreads();
+      if (tid < 64) {
+        // lane l holds the 16 contiguous digits [d0, d0 + 16) and walks them
+        // from the top; lanes go from the highest digits down (digits above
+        // 1 << nb are empty)
+        constexpr int kPer = (1 << kFinDigit) / 64;
+        const int d0 = (1 << kFinDigit) - kPer * (tid + 1);
+        uint32_t c[kPer];
 #pragma unroll
-      for (int j = 0; j < kU; ++j) {
-        const uint32_t i = i0 + j * kFinThreads + tid;
-        if (i < total) {
-          skey[i] = kk[j];
-          sidx[i] = ii[j];
+        for (int q = 0; q < kPer / 4; ++q) {
+          const v4i v = *reinterpret_cast<const v4i*>(&hist[d0 + 4 * q]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) c[4 * q + e] = (uint32_t)v[e];
         }
+        uint32_t tot = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) tot += c[j];
+        const uint32_t abv = wave_inclusive_sum(tot) - tot;
+        if (abv < want && want <= abv + tot) {
+          uint32_t acc = abv;
+#pragma unroll
+          for (int j = kPer - 1; j >= 0; --j) {
+            if (acc < want && want <= acc + c[j]) {
+              sm[0] = (uint32_t)(d0 + j);
+              sm[1] = acc;
+              sm[2] = c[j];
+            }
+            acc += c[j];
+          }
+        }
+      }
+      __syncthreads();
+      prefix |= sm[0] << shift;
+      want -= sm[1];
+      rem_bits = shift;
+      if (sm[2] == want) {  // this digit bin is kept whole
+        whole = true;
+        break;
+      }
+    }
+    // tau = prefix.  whole: keep key >= tau.  Otherwise keep key > tau and
+    // the `want` lowest positions among the copies of tau.
+    const uint32_t tau = prefix;
+    for (int i = tid; i < W4; i += kFinThreads) {
+      bitmap[i] = 0u;
+      tbits[i] = 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kCPer; ++j) {
+      if ((uint32_t)(tid + j * kFinThreads) < total) {
+        const uint32_t kk = ck[j], p = cp[j];
+        if (kk > tau || (whole && kk == tau)) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+        else if (kk == tau) atomicOr(&tbits[p >> 5], 1u << (p & 31));
       }
     }
     __syncthreads();
-    // Entries with bin > b* are all taken; resolve the rest inside bin b*.
-    tau = bstar << kBinShift;
-    want = (uint32_t)a.k - above;
-    radix_select_desc<kFinThreads, kDigitBits>(
-        [&](auto f) {
-          for (uint32_t i = tid; i < total; i += kFinThreads) f(skey[i]);
-        },
-        tau, kBinShift, want, whist, sm);
-  } else {
-    tau = 0u;
-    want = (uint32_t)a.k;
-    radix_select_desc<kFinThreads, kDigitBits>(
-        [&](auto f) {
-          for (int e = tid; e < n; e += kFinThreads) f(order_key(row[e]));
-        },
-        tau, 32, want, whist, sm);
+    const uint32_t written = whole ? bitmap_emit<kFinThreads>(bitmap, n, out, (uint32_t)a.k, sm)
+                                   : bitmap_select_emit<kFinThreads>(bitmap, tbits, n, want, out, (uint32_t)a.k, sm);
+    for (int j = (int)min(written, (uint32_t)a.k) + tid; j < a.k; j += kFinThreads) out[j] = -1;
+    return;
   }
-  // Mark {key > tau} and, separately, the copies of tau; of the copies the
-  // `want` lowest positions are taken (want >= 1 by the selection).
-  const int W4 = (((n + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
+
+  // Candidate list overflow: select straight from the score row.
+  uint32_t tau = 0u, want = (uint32_t)a.k;
+  radix_select_desc<kFinThreads, kDigitBits>(
+      [&](auto f) {
+        for (int e = tid; e < n; e += kFinThreads) f(order_key(row[e]));
+      },
+      tau, 32, want, whist, sm);
   for (int i = tid; i < W4; i += kFinThreads) {
     bitmap[i] = 0u;
     tbits[i] = 0u;
   }
   __syncthreads();
-  if (!direct) {
-    for (uint32_t i = tid; i < total; i += kFinThreads) {
-      const uint32_t key = skey[i], p = sidx[i];
-      if (key > tau) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
-      else if (key == tau) atomicOr(&tbits[p >> 5], 1u << (p & 31));
-    }
-  } else {
-    for (int e = tid; e < n; e += kFinThreads) {
-      const uint32_t key = order_key(row[e]);
-      if (key > tau) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-      else if (key == tau) atomicOr(&tbits[e >> 5], 1u << (e & 31));
-    }
+  for (int e = tid; e < n; e += kFinThreads) {
+    const uint32_t kk = order_key(row[e]);
+    if (kk > tau) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+    else if (kk == tau) atomicOr(&tbits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
   const uint32_t written = bitmap_select_emit<kFinThreads>(bitmap, tbits, n, want, out, (uint32_t)a.k, sm);
@@ -275,8 +330,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
 }
 
 size_t final_lds_bytes(int S_max, int k) {
-  return (((size_t)(kFinThreads / 64) << kDigitBits) + 64 + 2 * (size_t)((((S_max + 31) >> 5) + 3) & ~3) +
-          2 * cap_for(k)) * 4;
+  (void)k;
+  return (2 * (size_t)((((S_max + 31) >> 5) + 3) & ~3) + ((size_t)1 << kFinDigit) +
+          ((size_t)(kFinThreads / 64) << kDigitBits) + 64) * 4;
 }
 
 }  // namespace
