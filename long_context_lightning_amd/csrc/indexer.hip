@@ -26,6 +26,8 @@ constexpr int kKeysPerWave = 64;                               // keys per wave 
 constexpr int kKeysPerBlock = kWavesPerBlock * kKeysPerWave;   // keys per block per step
 constexpr int kKeysPerChunk = 4096;                            // keys streamed by one block
 
+__device__ float g_unit_scale = 1.0f;  // k-scale read when the cache has none (never written)
+
 __device__ __forceinline__ v8i load32(const uint8_t* p) {
   v4i lo = *reinterpret_cast<const v4i*>(p);
   v4i hi = *reinterpret_cast<const v4i*>(p + 16);
@@ -97,6 +99,10 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
 
   const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
   const float* ksb = a.k_scale ? a.k_scale + (size_t)rg.b * a.S_max : nullptr;
+  // Every key load is issued unconditionally (addresses clamped into
+  // [chunk0, kend), a missing k-scale read from a unit constant), so the
+  // compiler's memory-counter waits stay exact: the next step's keys stay in
+  // flight while the current step computes.
   auto load_keys = [&](int step, v8i (&kf)[4], float& ks) {
     const int kw = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave;
 #pragma unroll
@@ -105,11 +111,11 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
       kf[blk] = load32(kb + (size_t)s * kDI + 32 * g);
     }
     const int s_l = min(kw + lane, kend - 1);
-    ks = ksb ? ksb[s_l] : 1.0f;
+    ks = *(ksb ? ksb + s_l : &g_unit_scale);
   };
-  v8i kf_cur[4], kf_nxt[4];
-  float ks_cur, ks_nxt;
-  load_keys(0, kf_cur, ks_cur);
+  v8i kf_a[4], kf_b[4];
+  float ks_a, ks_b;
+  load_keys(0, kf_a, ks_a);
 
   // Query fragments (row = head 16m+c, bytes 32g..32g+31) and head weights of
   // the output rows this lane holds (heads 16m + 4g + i).
@@ -133,9 +139,11 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
         for (int i = 0; i < 4; ++i) wv[r][m][i] = 0.f;
     }
   }
+  // The row-dependent (conditional) loads above are complete before the
+  // step loop, so no wait inside it has to cover them.
+  __builtin_amdgcn_s_waitcnt(0);
 
-  for (int step = 0; step < nsteps; ++step) {
-    if (step + 1 < nsteps) load_keys(step + 1, kf_nxt, ks_nxt);
+  auto compute = [&](int step, const v8i (&kf)[4], float ks) {
     const int s_l = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave + lane;
     float x[NQ][4];
 #pragma unroll
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
         float acc = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const v4f d = mfma_fp8_16x16x128(qf[r][m], kf_cur[blk]);
+          const v4f d = mfma_fp8_16x16x128(qf[r][m], kf[blk]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], fmaxf(d[i], 0.f), acc);
         }
@@ -163,16 +171,30 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
       auto pf = __builtin_amdgcn_permlane32_swap(__float_as_uint(a01), __float_as_uint(a23), false, false);
       const float tot = __uint_as_float(pf[0]) + __uint_as_float(pf[1]);
       if (r < rg.nr && s_l < kend) {
-        const float v = tot * ks_cur;
-        out[(long long)r * a.ld + s_l] = (s_l <= pos[r]) ? v : -INFINITY;
+        // a store the compiler does not track: otherwise its pending count
+        // would force full memory waits in front of the next step's keys
+        const float v = (s_l <= pos[r]) ? tot * ks : -INFINITY;
+        store_u32_nowait(reinterpret_cast<uint32_t*>(out + (long long)r * a.ld + s_l), __float_as_uint(v));
       }
     }
-    if (step + 1 < nsteps) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) kf_cur[blk] = kf_nxt[blk];
-      ks_cur = ks_nxt;
-    }
+  };
+
+  // Two steps per trip with ping-pong key buffers (no register copies); the
+  // next step's loads are pinned ahead of the current step's MFMAs, so the
+  // waits in front of those MFMAs leave them in flight.  The trip body has
+  // no branch around a load (an odd last step is peeled after the loop).
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    load_keys(step + 1, kf_b, ks_b);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(step, kf_a, ks_a);
+    __builtin_amdgcn_sched_barrier(0);
+    load_keys(step + 2, kf_a, ks_a);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(step + 1, kf_b, ks_b);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (step < nsteps) compute(step, kf_a, ks_a);
 }
 
 // fp32 path (tiny configuration): one block per (row, 256-key tile), the query
