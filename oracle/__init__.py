@@ -19,10 +19,14 @@ the passage of the pages it follows:
   kernel 的交界面" list of what an implementation must define.
 * "NSA 与 DSA" (luowle page) section 3.2: public config 64 heads x 128 dims,
   top-k 2048, one shared indexer key per token.
+* ``quant``: the ``act_quant`` step of the ``Indexer`` code block (per-128
+  block e4m3fn codes with an ``amax / 448`` scale) and the key-cache append
+  ``k_cache[:bsz, start_pos:end_pos] = k_fp8``.
 
 """
 
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_times_512
+from .quant import cache_append, e4m3fn_nearest, quantize_blocks
 from .dsa import (
     query_positions,
     indexer_scores,
@@ -40,4 +44,7 @@ __all__ = [
     "topk_select",
     "sparse_mla",
     "dsa_forward",
+    "e4m3fn_nearest",
+    "quantize_blocks",
+    "cache_append",
 ]
