@@ -175,6 +175,38 @@ DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, fl
 DSA_API size_t dsa_forward_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H,
                                   int32_t topk, dsa_dtype index_dtype, dsa_dtype mla_dtype);
 
+/* Per-block fp8 quantisation of indexer inputs (the act_quant step of the
+ * "详解DSA" Indexer code block, applied there to q and to k before the key
+ * cache stores k; the "DSA计算流" section of that page keeps each key's scale
+ * in the cache and folds the q-scale into the head weights).  The pages do
+ * not print act_quant; the reading implemented: for every block of 128
+ * consecutive elements
+ *   scale        = max(amax, 2^-126) / 448           (fp32, amax = max |x|)
+ *   codes[e]     = e4m3fn(x[e] / scale)               (fp32 quotient)
+ * where e4m3fn() rounds to the nearest value, ties to the even code, gives
+ * 448 for a quotient beyond it and keeps the quotient's sign.
+ *
+ *   x      [rows, 128] BF16 or F32 (e.g. q as [T*64, 128])
+ *   codes  [rows, 128] uint8 e4m3fn codes;  scales [rows] fp32
+ * x must be 16-byte aligned, codes and scales 4-byte aligned; rows >= 0.
+ * A q_scale produced here is the q_scale argument of dsa_indexer_scores. */
+DSA_API dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_t rows,
+                                uint8_t* codes, float* scales, hipStream_t stream);
+
+/* Indexer key-cache append (the k_cache[:bsz, start_pos:end_pos] = k_fp8
+ * and k_scale_cache lines of the "详解DSA" Indexer code block): the q_len
+ * new keys of sequence b are quantised as in dsa_indexer_quantize and
+ * written at positions L_b - q_len + i, i < q_len, with
+ * L_b = clamp(seq_lens[b], 0, S_max) (so end_pos = L_b, the convention of
+ * the query positions); positions below zero are skipped and no other entry
+ * of either cache is touched.
+ *
+ *   k_new          [B, q_len, 128] BF16 or F32 (16-byte aligned)
+ *   k_cache        [B, S_max, 128] uint8 e4m3fn codes (4-byte aligned)
+ *   k_scale_cache  [B, S_max] fp32 (4-byte aligned) */
+DSA_API dsa_status dsa_indexer_cache_append(const dsa_geom* geom, const void* k_new, dsa_dtype k_dtype,
+                                    uint8_t* k_cache, float* k_scale_cache, hipStream_t stream);
+
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);
 

@@ -53,6 +53,8 @@ def load(path=None):
         "dsa_forward": (i32, [gp, i32, i32, f32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                               vp]),
         "dsa_forward_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "dsa_indexer_quantize": (i32, [vp, i32, i64, vp, vp, vp]),
+        "dsa_indexer_cache_append": (i32, [gp, vp, i32, vp, vp, vp]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -66,7 +68,7 @@ def load(path=None):
 
 ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla",
                  "dsa_sparse_mla_workspace_size", "dsa_forward", "dsa_forward_workspace_size",
-                 "dsa_status_string", "dsa_version")
+                 "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_status_string", "dsa_version")
 
 
 def _ptr(t):
@@ -239,3 +241,44 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
                          ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dsa_forward")
     return idx, out, lse
+
+
+def _quant_dtype(t):
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"quantisation input dtype {t.dtype} unsupported")
+
+
+def indexer_quantize(x, codes=None, scales=None, stream=None):
+    """dsa_indexer_quantize: x [..., 128] bf16/fp32 -> (uint8 codes [..., 128], fp32 scales [...])."""
+    lib = load()
+    _dev(x, "x", (torch.bfloat16, torch.int16, torch.uint16, torch.float32))
+    _need(x.dim() >= 1 and x.shape[-1] == 128, "x must be [..., 128]")
+    rows = x.numel() // 128
+    if codes is None:
+        codes = torch.empty(tuple(x.shape), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]), dtype=torch.float32, device=x.device)
+    _dev(codes, "codes", (torch.uint8, _FP8))
+    _dev(scales, "scales", (torch.float32,))
+    _need(codes.numel() == x.numel() and scales.numel() == rows, "codes / scales size mismatch")
+    st = lib.dsa_indexer_quantize(_ptr(x), _quant_dtype(x), rows, _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "dsa_indexer_quantize")
+    return codes, scales
+
+
+def indexer_cache_append(geom, k_new, k_cache, k_scale_cache, stream=None):
+    """dsa_indexer_cache_append: quantise k_new [B, q_len, 128] into the caches in place."""
+    lib = load()
+    _dev(k_new, "k_new", (torch.bfloat16, torch.int16, torch.uint16, torch.float32))
+    _dev(k_cache, "k_cache", (torch.uint8, _FP8))
+    _dev(k_scale_cache, "k_scale_cache", (torch.float32,))
+    _need(tuple(k_new.shape) == (geom.B, geom.q_len, 128), "k_new must be [B, q_len, 128]")
+    _need(tuple(k_cache.shape) == (geom.B, geom.S_max, 128), "k_cache must be [B, S_max, 128]")
+    _need(tuple(k_scale_cache.shape) == (geom.B, geom.S_max), "k_scale_cache must be [B, S_max]")
+    st = lib.dsa_indexer_cache_append(ctypes.byref(geom), _ptr(k_new), _quant_dtype(k_new), _ptr(k_cache),
+                                      _ptr(k_scale_cache), _stream(stream))
+    _check(st, "dsa_indexer_cache_append")
+    return k_cache, k_scale_cache

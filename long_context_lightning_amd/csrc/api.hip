@@ -310,6 +310,37 @@ dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_s
   return hip_status(run_mla(ma, mla_dtype == DSA_BF16, stream));
 }
 
+dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_t rows, uint8_t* codes, float* scales,
+                                hipStream_t stream) {
+  if (rows < 0) return DSA_ERR_INVALID_ARG;
+  if (x_dtype != DSA_BF16 && x_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (rows == 0) return DSA_OK;
+  if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 4) || !aligned(scales, 4))
+    return DSA_ERR_INVALID_ARG;
+  QuantArgs a{};
+  a.x = x;
+  a.rows = rows;
+  a.codes = codes;
+  a.scales = scales;
+  return hip_status(launch_quantize(a, x_dtype == DSA_BF16, stream));
+}
+
+dsa_status dsa_indexer_cache_append(const dsa_geom* geom, const void* k_new, dsa_dtype k_dtype, uint8_t* k_cache,
+                                    float* k_scale_cache, hipStream_t stream) {
+  if (!geom_ok(geom) || !k_new || !k_cache || !k_scale_cache) return DSA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(k_cache, 4) || !aligned(k_scale_cache, 4)) return DSA_ERR_INVALID_ARG;
+  if (k_dtype != DSA_BF16 && k_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  QuantArgs a{};
+  a.x = k_new;
+  a.rows = rows_of(geom);
+  a.codes = k_cache;
+  a.scales = k_scale_cache;
+  a.seq_lens = geom->seq_lens;
+  a.q_len = geom->q_len;
+  a.S_max = geom->S_max;
+  return hip_status(launch_cache_append(a, k_dtype == DSA_BF16, stream));
+}
+
 const char* dsa_status_string(dsa_status s) {
   switch (s) {
     case DSA_OK: return "DSA_OK";

@@ -200,6 +200,20 @@ struct TopkArgs {
   int ws_zeroed;          // the counters in ws are already zero (cleared by the indexer launch)
 };
 
+// Per-block fp8 quantisation (launch_quantize: rows -> codes/scales;
+// launch_cache_append: row b*q_len+i -> cache position
+// clamp(seq_lens[b]) - q_len + i).
+struct QuantArgs {
+  const void* x;            // [rows, 128] bf16 or fp32
+  long long rows;
+  uint8_t* codes;           // [rows, 128], or the key cache [B, S_max, 128]
+  float* scales;            // [rows], or the scale cache [B, S_max]
+  const int32_t* seq_lens;  // cache append only
+  int q_len, S_max;         // cache append only
+};
+hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_cache_append(const QuantArgs& a, bool bf16, hipStream_t s);
+
 size_t topk_workspace_bytes(int row_count, int S_max, int k);
 // The words of a top-k workspace that must be zero before launch_topk.
 void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* stride_words, int* words);

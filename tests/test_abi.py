@@ -97,3 +97,21 @@ def test_forward_workspace_sizes_are_consistent():
     pre = lib.dsa_forward_workspace_size(1, 65536, 65536, 128, 2048, 2, 1)
     assert pre < 65536 * 65536 * 4 // 4         # streaming prefill never holds T x S
     assert lib.dsa_forward_workspace_size(0, 1, 1, 1, 1, 2, 1) == 0
+
+
+def test_quantize_and_cache_append_validation():
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    assert lib.dsa_indexer_quantize(P(FAKE), 1, -1, P(FAKE), P(FAKE), None) == 1        # negative rows
+    assert lib.dsa_indexer_quantize(P(FAKE), 2, 4, P(FAKE), P(FAKE), None) == 2         # fp8 input
+    assert lib.dsa_indexer_quantize(P(FAKE + 8), 1, 4, P(FAKE), P(FAKE), None) == 1     # misaligned x
+    assert lib.dsa_indexer_quantize(P(FAKE), 1, 4, None, P(FAKE), None) == 1            # null codes
+    assert lib.dsa_indexer_quantize(P(FAKE), 0, 4, P(FAKE), P(FAKE + 2), None) == 1     # misaligned scales
+    assert lib.dsa_indexer_quantize(P(FAKE), 1, 0, P(FAKE), P(FAKE), None) == 0         # nothing to do
+    g = _geom(B=2, q_len=3, S=16)
+    assert lib.dsa_indexer_cache_append(None, P(FAKE), 1, P(FAKE), P(FAKE), None) == 1
+    assert lib.dsa_indexer_cache_append(ctypes.byref(g), P(FAKE), 2, P(FAKE), P(FAKE), None) == 2
+    assert lib.dsa_indexer_cache_append(ctypes.byref(g), P(FAKE + 4), 1, P(FAKE), P(FAKE), None) == 1
+    assert lib.dsa_indexer_cache_append(ctypes.byref(g), P(FAKE), 1, None, P(FAKE), None) == 1
+    bad = _geom(B=1, q_len=20, S=16)
+    assert lib.dsa_indexer_cache_append(ctypes.byref(bad), P(FAKE), 1, P(FAKE), P(FAKE), None) == 1
