@@ -191,6 +191,9 @@ def main():
                 "traffic": measured_traffic("indexer_fp8_decode128k")}
     del scores
 
+    # ------------------------------------------- fp8 quantisation / append
+    quant = bench_quant(lcl, torch, dev, stream, evict, wl)
+
     # --------------------------------------------------------- prefill 64K
     prefill = None
     if not args.no_prefill:
@@ -222,10 +225,58 @@ def main():
                    "llc_scrub_between_steps": not args.no_scrub},
         "roofline": roofline,
         "stages": stages,
+        "quantize": quant,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_quant(lcl, torch, dev, stream, evict, wl):
+    """The indexer's fp8 quantisation kernels: the per-step key-cache append
+    and query quantisation of the 128K decode step, and the query
+    quantisation of a 64K-token prefill ([65536*64, 128] bf16 in, codes and
+    scales out); each is timed as single launches, each after a last-level
+    cache eviction (median of 20, or 10 for the prefill shape)."""
+    T = wl.T
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def timed(fn, reps=20):
+        ts = []
+        for _ in range(reps + 3):
+            evict()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]) * 1e3)
+        ts = sorted(ts[3:])
+        return ts[len(ts) // 2]
+
+    seq = torch.full((wl.B,), wl.S_max, dtype=torch.int32, device=dev)
+    geom = lcl.make_geom(wl.B, wl.q_len, wl.S_max, seq)
+    k_new = torch.randn((wl.B, wl.q_len, 128), generator=g, device=dev).to(torch.bfloat16)
+    kc = torch.zeros((wl.B, wl.S_max, 128), dtype=torch.uint8, device=dev)
+    kcs = torch.zeros((wl.B, wl.S_max), dtype=torch.float32, device=dev)
+    app_us = timed(lambda: lcl.indexer_cache_append(geom, k_new, kc, kcs))
+    q_dec = torch.randn((T * 64, 128), generator=g, device=dev).to(torch.bfloat16)
+    qd_us = timed(lambda: lcl.indexer_quantize(q_dec))
+    del kc, kcs
+    rows = 65536 * 64
+    q_pf = torch.randn((rows, 128), generator=g, device=dev).to(torch.bfloat16)
+    codes = torch.empty((rows, 128), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows,), dtype=torch.float32, device=dev)
+    qp_us = timed(lambda: lcl.indexer_quantize(q_pf, codes=codes, scales=scales), reps=10)
+    qp_bytes = rows * (128 * 2 + 128 + 4)
+    qp_gbs = qp_bytes / (qp_us * 1e-6) / 1e9
+    log(f"quantize: decode128k key append {app_us:.1f} us, decode128k q ({T * 64} rows) {qd_us:.1f} us; "
+        f"prefill64k q ({rows} rows bf16) {qp_us:.1f} us = {qp_gbs:.1f} GB/s ({qp_gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+    del q_pf, codes, scales
+    return {"decode128k_key_append_us": round(app_us, 2), "decode128k_q_quantize_us": round(qd_us, 2),
+            "prefill64k_q_quantize": {"us": round(qp_us, 2), "bytes": qp_bytes, "GB_s": round(qp_gbs, 1),
+                                      "hbm_frac": round(qp_gbs / HBM_PEAK_GBS, 4)}}
 
 
 def measured_traffic(name):

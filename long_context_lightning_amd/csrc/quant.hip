@@ -10,12 +10,14 @@
 // the fp32 quotient x / scale rounded to the nearest e4m3fn value (ties to
 // the even code, 448 for a quotient past it, the quotient's sign kept).
 //
-// HBM-bound streaming: a 32-lane half-wave owns one block; lane j loads
-// elements 4j..4j+3 (8 bytes of bf16 or 16 of fp32), the block maximum comes
-// from five xor-shuffles inside the half-wave, and each lane stores its four
-// codes as one 4-byte word, so a block's 128 codes are one coalesced
-// 128-byte store.  Grid-stride over blocks; every lane of a half-wave takes
-// the same trip count, so the shuffles never see an inactive partner.
+// HBM-bound streaming: a 32-lane half-wave owns one block at a time; lane j
+// loads elements 4j..4j+3 (8 bytes of bf16 or 16 of fp32), the block maximum
+// comes from five xor-shuffles inside the half-wave, and each lane stores
+// its four codes as one 4-byte word, so a block's 128 codes are one
+// coalesced 128-byte store.  Grid-stride over blocks, kU blocks per trip;
+// every lane of a half-wave takes the same trips and computes every block of
+// a trip (the stores are what is skipped), so the shuffles never see an
+// inactive partner.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -25,34 +27,6 @@ namespace {
 constexpr int kBlock = 128;
 constexpr int kThreads = 256;
 constexpr int kBlocksPerCta = kThreads / 32;
-
-// fp32 -> e4m3fn code, round to nearest even, saturating at 448, sign kept.
-// |v| < 2^-6 is the subnormal range (step 2^-9): the code is the rounded
-// multiple of 2^-9 (8 meaning the smallest normal, whose code is also 8).
-// Otherwise the 23-bit fp32 mantissa is rounded to 3 bits with the carry
-// moving into the exponent.
-__device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (!(a < 448.0f)) {
-    code = 0x7Eu;
-  } else if (a < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    uint32_t e = (ua >> 23) - 120u;  // biased e4m3 exponent: (e8 - 127) + 7
-    uint32_t m = (ua >> 20) & 7u;
-    const uint32_t rem = ua & 0xFFFFFu;
-    m += (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ? 1u : 0u;
-    if (m == 8u) {
-      m = 0u;
-      ++e;
-    }
-    code = min((e << 3) | m, 0x7Eu);
-  }
-  return code | sign;
-}
 
 template <bool BF16>
 __device__ __forceinline__ void load4(const void* x, long long blk, int j, float (&v)[4]) {
@@ -71,50 +45,55 @@ __device__ __forceinline__ void load4(const void* x, long long blk, int j, float
   }
 }
 
-// Quantises block blk in the calling half-wave; returns the lane's packed
-// codes and (in every lane) the block scale.
-template <bool BF16>
-__device__ __forceinline__ uint32_t quant_block(const void* x, long long blk, int j, float& scale) {
-  float v[4];
-  load4<BF16>(x, blk, j, v);
+// Codes of the lane's four elements of one block (its scale in every lane
+// of the half-wave).  The quotients, clamped to +-448 (the fp32 rounding of
+// the scale can put the block maximum a hair above it), go through the
+// gfx950 packed fp32 -> e4m3fn conversion (round to nearest even), two per
+// instruction.
+__device__ __forceinline__ uint32_t quant4(const float (&v)[4], float& scale) {
   float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
   amax = fmaxf(amax, 0x1p-126f);
   scale = __fdiv_rn(amax, 448.0f);
-  uint32_t packed = 0;
+  float qv[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) packed |= e4m3fn_rne(__fdiv_rn(v[e], scale)) << (8 * e);
-  return packed;
+  for (int e = 0; e < 4; ++e) qv[e] = __builtin_amdgcn_fmed3f(__fdiv_rn(v[e], scale), -448.0f, 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(qv[0], qv[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(qv[2], qv[3], lo, true);
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_quantize(QuantArgs a) {
+// Each half-wave takes kU blocks per trip (blk, blk + stride, ...), all
+// loads issued first (indices clamped into range, out-of-range results not
+// stored), so every lane keeps kU loads in flight.
+constexpr int kU = 4;
+
+template <bool BF16, bool APPEND>
+__global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
   const int j = threadIdx.x & 31;
   const long long first = (long long)blockIdx.x * kBlocksPerCta + (threadIdx.x >> 5);
   const long long stride = (long long)gridDim.x * kBlocksPerCta;
-  for (long long blk = first; blk < a.rows; blk += stride) {
-    float scale;
-    const uint32_t packed = quant_block<BF16>(a.x, blk, j, scale);
-    reinterpret_cast<uint32_t*>(a.codes + blk * kBlock)[j] = packed;
-    if (j == 0) a.scales[blk] = scale;
-  }
-}
-
-// Row blk = b * q_len + i of the new keys goes to position
-// clamp(seq_lens[b], 0, S_max) - q_len + i of sequence b (skipped if negative).
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_cache_append(QuantArgs a) {
-  const int j = threadIdx.x & 31;
-  const long long first = (long long)blockIdx.x * kBlocksPerCta + (threadIdx.x >> 5);
-  const long long stride = (long long)gridDim.x * kBlocksPerCta;
-  for (long long blk = first; blk < a.rows; blk += stride) {
-    const int b = (int)(blk / a.q_len), i = (int)(blk - (long long)b * a.q_len);
-    const int s = clamped_len(a.seq_lens, b, a.S_max) - a.q_len + i;
-    float scale;
-    const uint32_t packed = quant_block<BF16>(a.x, blk, j, scale);
-    if (s >= 0) {
-      const long long dst = (long long)b * a.S_max + s;
+  for (long long blk0 = first; blk0 < a.rows; blk0 += kU * stride) {
+    float v[kU][4];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const long long blk = blk0 + u * stride;
+      load4<BF16>(a.x, blk < a.rows ? blk : a.rows - 1, j, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const long long blk = blk0 + u * stride;
+      float scale;
+      const uint32_t packed = quant4(v[u], scale);
+      if (blk >= a.rows) continue;
+      long long dst = blk;
+      if (APPEND) {
+        // row b*q_len + i -> position clamp(seq_lens[b], 0, S_max) - q_len + i
+        const int b = (int)(blk / a.q_len), i = (int)(blk - (long long)b * a.q_len);
+        const int s = clamped_len(a.seq_lens, b, a.S_max) - a.q_len + i;
+        if (s < 0) continue;
+        dst = (long long)b * a.S_max + s;
+      }
       reinterpret_cast<uint32_t*>(a.codes + dst * kBlock)[j] = packed;
       if (j == 0) a.scales[dst] = scale;
     }
@@ -131,16 +110,16 @@ unsigned grid_for(long long rows) {
 hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const dim3 grid(grid_for(a.rows)), block(kThreads);
-  if (bf16) hipLaunchKernelGGL(k_quantize<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(k_quantize<false>, grid, block, 0, stream, a);
+  if (bf16) hipLaunchKernelGGL((k_quant<true, false>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((k_quant<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_cache_append(const QuantArgs& a, bool bf16, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   const dim3 grid(grid_for(a.rows)), block(kThreads);
-  if (bf16) hipLaunchKernelGGL(k_cache_append<true>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(k_cache_append<false>, grid, block, 0, stream, a);
+  if (bf16) hipLaunchKernelGGL((k_quant<true, true>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((k_quant<false, true>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
