@@ -22,11 +22,15 @@ the passage of the pages it follows:
 * ``quant``: the ``act_quant`` step of the ``Indexer`` code block (per-128
   block e4m3fn codes with an ``amax / 448`` scale) and the key-cache append
   ``k_cache[:bsz, start_pos:end_pos] = k_fp8``.
+* ``paged``: paged caches (charlestar page, "Prefill 与 decode 中发生了什么"
+  and "Top-k 是算法与 kernel 的交界面"): a block table maps a logical
+  position to a page and an offset.
 
 """
 
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_times_512
 from .quant import cache_append, e4m3fn_nearest, quantize_blocks
+from .paged import gather_pages, scatter_pages
 from .dsa import (
     query_positions,
     indexer_scores,
@@ -47,4 +51,6 @@ __all__ = [
     "e4m3fn_nearest",
     "quantize_blocks",
     "cache_append",
+    "gather_pages",
+    "scatter_pages",
 ]
