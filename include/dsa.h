@@ -207,6 +207,82 @@ DSA_API dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_
 DSA_API dsa_status dsa_indexer_cache_append(const dsa_geom* geom, const void* k_new, dsa_dtype k_dtype,
                                     uint8_t* k_cache, float* k_scale_cache, hipStream_t stream);
 
+/* ---------------------------------------------------------------------
+ * Paged caches.  The charlestar page ("DeepSeek V3.2 稀疏注意力") raises
+ * paged KV twice: in "Prefill 与 decode 中发生了什么" (Decode), top-k
+ * positions must be mapped to physical KV pages and the selected entries
+ * spread over many pages; in "Top-k 是算法与 kernel 的交界面", a logical
+ * position becomes a page and an offset.  Here a cache is a POOL of
+ * num_pages pages of page_size tokens shared by all sequences, plus a block
+ * table: token s of sequence b lives in row s % page_size of page
+ * block_table[b * max_pages + s / page_size].  Every result equals the
+ * contiguous call's on the cache that the table describes (same kernels,
+ * same arithmetic); seq_lens, positions, the causal rule and idx stay
+ * LOGICAL positions.
+ *
+ *   block_table  DEVICE [B, max_pages] int32 page ids (4-byte aligned)
+ *   page_size    a power of two, 64 <= page_size <= 65536
+ *   max_pages    >= 1 with max_pages * page_size >= S_max, B * max_pages < 2^31
+ *   num_pages    >= 1 with num_pages * page_size < 2^31 (pool rows fit int32)
+ * Only the table entries of pages holding tokens s < clamp(seq_lens[b], 0,
+ * S_max) are read.  They should lie in [0, num_pages); the kernels clamp any
+ * other id into that range, so a bad entry reads or writes a wrong page of
+ * the pool but never memory outside it.  Pages may be shared or reordered
+ * freely between sequences.  The library keeps no pointer to the table. */
+typedef struct {
+  const int32_t* block_table;
+  int32_t max_pages;
+  int32_t page_size;
+  int64_t num_pages;
+} dsa_pages;
+
+/* dsa_indexer_scores on paged fp8 (or f32) key caches:
+ *   k_pool        [num_pages, page_size, 128] same dtype as q
+ *   k_scale_pool  [num_pages, page_size] fp32 or NULL (= 1)
+ * Other arguments, results and errors as in dsa_indexer_scores; a NULL or
+ * invalid `pages` gives DSA_ERR_INVALID_ARG. */
+DSA_API dsa_status dsa_indexer_scores_paged(const dsa_geom* geom, const dsa_pages* pages,
+                              const void* q, dsa_dtype q_dtype, const float* q_scale,
+                              const void* w, dsa_dtype w_dtype,
+                              const void* k_pool, dsa_dtype k_dtype, const float* k_scale_pool,
+                              int32_t row_begin, int32_t row_count,
+                              float* scores, int64_t ld, hipStream_t stream);
+
+/* dsa_sparse_mla on a paged latent cache:
+ *   kv_pool [num_pages, page_size, 576] BF16 or F32 (the dtype of q)
+ * idx holds logical positions as in dsa_sparse_mla; they are translated to
+ * pool rows inside the workspace before the gather, so the attention reads
+ * the pool with no table look-up per entry.
+ * ws >= dsa_sparse_mla_paged_workspace_size(...) bytes (256-byte aligned). */
+DSA_API dsa_status dsa_sparse_mla_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k,
+                          float sm_scale, const void* q, dsa_dtype dtype, const void* kv_pool,
+                          const int32_t* idx, void* out, float* lse,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_sparse_mla_paged_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t k,
+                                     dsa_dtype dtype);
+
+/* dsa_forward on paged caches (index_k_pool / index_k_scale_pool as in
+ * dsa_indexer_scores_paged, mla_kv_pool as in dsa_sparse_mla_paged).
+ * Every shape scores into the workspace (no streamed prefill).
+ * ws >= dsa_forward_paged_workspace_size(...) bytes. */
+DSA_API dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H,
+                       float sm_scale,
+                       const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                       const void* index_w, dsa_dtype index_w_dtype,
+                       const void* index_k_pool, const float* index_k_scale_pool,
+                       const void* mla_q, const void* mla_kv_pool, dsa_dtype mla_dtype,
+                       int32_t* idx_out, void* out, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_forward_paged_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H,
+                                  int32_t topk, dsa_dtype index_dtype, dsa_dtype mla_dtype);
+
+/* dsa_indexer_cache_append into paged pools: the new key of position s of
+ * sequence b goes to pool row s % page_size of its page.
+ *   k_pool [num_pages, page_size, 128] uint8;  k_scale_pool [num_pages, page_size] fp32 */
+DSA_API dsa_status dsa_indexer_cache_append_paged(const dsa_geom* geom, const dsa_pages* pages,
+                                    const void* k_new, dsa_dtype k_dtype,
+                                    uint8_t* k_pool, float* k_scale_pool, hipStream_t stream);
+
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);
 

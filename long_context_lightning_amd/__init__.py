@@ -33,6 +33,11 @@ class Geom(ctypes.Structure):
                 ("seq_lens", ctypes.c_void_p)]
 
 
+class Pages(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int64)]
+
+
 def load(path=None):
     """Load libdsa.so (once).  Raises if it is missing or incomplete."""
     global _lib
@@ -44,6 +49,7 @@ def load(path=None):
     lib = ctypes.CDLL(path)
     vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     gp = ctypes.POINTER(Geom)
+    pp = ctypes.POINTER(Pages)
     sig = {
         "dsa_indexer_scores": (i32, [gp, vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, vp, i64, vp]),
         "dsa_topk": (i32, [gp, vp, i64, i32, i32, i32, vp, vp, sz, vp]),
@@ -55,6 +61,13 @@ def load(path=None):
         "dsa_forward_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "dsa_indexer_quantize": (i32, [vp, i32, i64, vp, vp, vp]),
         "dsa_indexer_cache_append": (i32, [gp, vp, i32, vp, vp, vp]),
+        "dsa_indexer_scores_paged": (i32, [gp, pp, vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, vp, i64, vp]),
+        "dsa_sparse_mla_paged": (i32, [gp, pp, i32, i32, f32, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "dsa_sparse_mla_paged_workspace_size": (sz, [i32, i32, i32, i32, i32]),
+        "dsa_forward_paged": (i32, [gp, pp, i32, i32, f32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp,
+                                    vp, sz, vp]),
+        "dsa_forward_paged_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "dsa_indexer_cache_append_paged": (i32, [gp, pp, vp, i32, vp, vp, vp]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -68,7 +81,10 @@ def load(path=None):
 
 ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla",
                  "dsa_sparse_mla_workspace_size", "dsa_forward", "dsa_forward_workspace_size",
-                 "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_status_string", "dsa_version")
+                 "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_indexer_scores_paged",
+                 "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
+                 "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_status_string",
+                 "dsa_version")
 
 
 def _ptr(t):
@@ -130,9 +146,24 @@ def make_geom(B, q_len, S_max, seq_lens):
     return Geom(B, q_len, S_max, seq_lens.data_ptr())
 
 
+def make_pages(block_table, page_size, num_pages):
+    """Page-table struct; ``block_table`` is an int32 device tensor [B, max_pages] (kept alive by the caller)."""
+    _dev(block_table, "block_table", (torch.int32,))
+    _need(block_table.dim() == 2, "block_table must be [B, max_pages]")
+    return Pages(block_table.data_ptr(), block_table.shape[1], page_size, num_pages)
+
+
+def _cache_shape(geom, pages, tail):
+    """Expected shape of a cache: [B, S_max, *tail], or the pool [num_pages, page_size, *tail]."""
+    if pages is None:
+        return (geom.B, geom.S_max) + tail
+    return (pages.num_pages, pages.page_size) + tail
+
+
 def indexer_scores(geom, q, w, k, k_scale=None, q_scale=None, row_begin=0, row_count=None, scores=None,
-                   stream=None):
-    """dsa_indexer_scores: returns fp32 scores [row_count, S_max]."""
+                   stream=None, pages=None):
+    """dsa_indexer_scores (dsa_indexer_scores_paged when ``pages`` is given,
+    with ``k`` / ``k_scale`` the page pools): returns fp32 scores [row_count, S_max]."""
     lib = load()
     T = geom.B * geom.q_len
     row_count = T - row_begin if row_count is None else row_count
@@ -140,9 +171,9 @@ def indexer_scores(geom, q, w, k, k_scale=None, q_scale=None, row_begin=0, row_c
     _dev(k, "k", (_FP8, torch.uint8, torch.float32))
     _dev(w, "w", (torch.bfloat16, torch.int16, torch.uint16, torch.float32))
     _need(tuple(q.shape) == (T, 64, 128), f"q shape {tuple(q.shape)} != {(T, 64, 128)}")
-    _need(tuple(k.shape) == (geom.B, geom.S_max, 128), "k shape mismatch")
+    _need(tuple(k.shape) == _cache_shape(geom, pages, (128,)), "k shape mismatch")
     _need(tuple(w.shape) == (T, 64), "w shape mismatch")
-    for name, s, shape in (("k_scale", k_scale, (geom.B, geom.S_max)), ("q_scale", q_scale, (T, 64))):
+    for name, s, shape in (("k_scale", k_scale, _cache_shape(geom, pages, ())), ("q_scale", q_scale, (T, 64))):
         if s is not None:
             _dev(s, name, (torch.float32,))
             _need(tuple(s.shape) == shape, f"{name} shape mismatch")
@@ -150,10 +181,13 @@ def indexer_scores(geom, q, w, k, k_scale=None, q_scale=None, row_begin=0, row_c
         scores = torch.empty((row_count, geom.S_max), dtype=torch.float32, device=q.device)
     _dev(scores, "scores", (torch.float32,))
     _need(scores.dim() == 2 and scores.shape[0] >= row_count, "scores too small")
-    st = lib.dsa_indexer_scores(ctypes.byref(geom), _ptr(q), _index_dtype(q), _ptr(q_scale), _ptr(w), _w_dtype(w),
-                                _ptr(k), _index_dtype(k), _ptr(k_scale), row_begin, row_count, _ptr(scores),
-                                scores.stride(0), _stream(stream))
-    _check(st, "dsa_indexer_scores")
+    args = (_ptr(q), _index_dtype(q), _ptr(q_scale), _ptr(w), _w_dtype(w), _ptr(k), _index_dtype(k), _ptr(k_scale),
+            row_begin, row_count, _ptr(scores), scores.stride(0), _stream(stream))
+    if pages is None:
+        _check(lib.dsa_indexer_scores(ctypes.byref(geom), *args), "dsa_indexer_scores")
+    else:
+        _check(lib.dsa_indexer_scores_paged(ctypes.byref(geom), ctypes.byref(pages), *args),
+               "dsa_indexer_scores_paged")
     return scores
 
 
@@ -183,15 +217,20 @@ def sparse_mla_workspace_size(B, q_len, H, k, dtype):
     return int(load().dsa_sparse_mla_workspace_size(B, q_len, H, k, dtype))
 
 
-def sparse_mla(geom, q, kv, idx, sm_scale, out=None, lse=None, ws=None, want_lse=True, stream=None):
-    """dsa_sparse_mla: returns (out [T, H, 512], lse [T, H] or None)."""
+def sparse_mla_paged_workspace_size(B, q_len, H, k, dtype):
+    return int(load().dsa_sparse_mla_paged_workspace_size(B, q_len, H, k, dtype))
+
+
+def sparse_mla(geom, q, kv, idx, sm_scale, out=None, lse=None, ws=None, want_lse=True, stream=None, pages=None):
+    """dsa_sparse_mla (dsa_sparse_mla_paged when ``pages`` is given, with
+    ``kv`` the page pool): returns (out [T, H, 512], lse [T, H] or None)."""
     lib = load()
     T = geom.B * geom.q_len
     _dev(q, "q", (torch.bfloat16, torch.float32, torch.int16, torch.uint16))
     _dev(kv, "kv", (q.dtype,))
     _dev(idx, "idx", (torch.int32,))
     _need(q.dim() == 3 and q.shape[0] == T and q.shape[2] == 576, "q must be [T, H, 576]")
-    _need(tuple(kv.shape) == (geom.B, geom.S_max, 576), "kv must be [B, S_max, 576]")
+    _need(tuple(kv.shape) == _cache_shape(geom, pages, (576,)), "kv shape mismatch")
     _need(idx.dim() == 2 and idx.shape[0] == T, "idx must be [T, k]")
     H, k = q.shape[1], idx.shape[1]
     if out is None:
@@ -199,12 +238,18 @@ def sparse_mla(geom, q, kv, idx, sm_scale, out=None, lse=None, ws=None, want_lse
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     dt = _mla_dtype(q)
-    need = sparse_mla_workspace_size(geom.B, geom.q_len, H, k, dt)
+    if pages is None:
+        need = sparse_mla_workspace_size(geom.B, geom.q_len, H, k, dt)
+    else:
+        need = sparse_mla_paged_workspace_size(geom.B, geom.q_len, H, k, dt)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = lib.dsa_sparse_mla(ctypes.byref(geom), H, k, float(sm_scale), _ptr(q), dt, _ptr(kv), _ptr(idx), _ptr(out),
-                            _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "dsa_sparse_mla")
+    args = (H, k, float(sm_scale), _ptr(q), dt, _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(stream))
+    if pages is None:
+        _check(lib.dsa_sparse_mla(ctypes.byref(geom), *args), "dsa_sparse_mla")
+    else:
+        _check(lib.dsa_sparse_mla_paged(ctypes.byref(geom), ctypes.byref(pages), *args), "dsa_sparse_mla_paged")
     return out, lse
 
 
@@ -212,9 +257,15 @@ def forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype):
     return int(load().dsa_forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype))
 
 
+def forward_paged_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype):
+    return int(load().dsa_forward_paged_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype))
+
+
 def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, index_k_scale=None,
-            index_q_scale=None, idx=None, out=None, lse=None, ws=None, want_lse=True, stream=None):
-    """dsa_forward: indexer -> top-k -> sparse MLA.  Returns (idx, out, lse)."""
+            index_q_scale=None, idx=None, out=None, lse=None, ws=None, want_lse=True, stream=None, pages=None):
+    """dsa_forward: indexer -> top-k -> sparse MLA (dsa_forward_paged when
+    ``pages`` is given, with ``index_k``, ``index_k_scale`` and ``mla_kv`` the
+    page pools).  Returns (idx, out, lse)."""
     lib = load()
     T = geom.B * geom.q_len
     H = mla_q.shape[1]
@@ -226,20 +277,23 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
     if lse is None and want_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
     idt, mdt = _index_dtype(index_q), _mla_dtype(mla_q)
-    need = forward_workspace_size(geom.B, geom.q_len, geom.S_max, H, topk_k, idt, mdt)
+    size_fn = forward_workspace_size if pages is None else forward_paged_workspace_size
+    need = size_fn(geom.B, geom.q_len, geom.S_max, H, topk_k, idt, mdt)
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     for name, t in (("index_q", index_q), ("index_w", index_w), ("index_k", index_k), ("mla_q", mla_q),
                     ("mla_kv", mla_kv), ("idx", idx), ("out", out)):
         _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
-    _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == (geom.B, geom.S_max, 128),
+    _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == _cache_shape(geom, pages, (128,)),
           "indexer shapes mismatch")
-    _need(tuple(mla_kv.shape) == (geom.B, geom.S_max, 576) and mla_q.shape[0] == T, "MLA shapes mismatch")
-    st = lib.dsa_forward(ctypes.byref(geom), topk_k, H, float(sm_scale), _ptr(index_q), idt, _ptr(index_q_scale),
-                         _ptr(index_w), _w_dtype(index_w), _ptr(index_k), _ptr(index_k_scale), _ptr(mla_q),
-                         _ptr(mla_kv), mdt, _ptr(idx), _ptr(out), _ptr(lse), _ptr(ws),
-                         ws.numel() * ws.element_size(), _stream(stream))
-    _check(st, "dsa_forward")
+    _need(tuple(mla_kv.shape) == _cache_shape(geom, pages, (576,)) and mla_q.shape[0] == T, "MLA shapes mismatch")
+    args = (topk_k, H, float(sm_scale), _ptr(index_q), idt, _ptr(index_q_scale), _ptr(index_w), _w_dtype(index_w),
+            _ptr(index_k), _ptr(index_k_scale), _ptr(mla_q), _ptr(mla_kv), mdt, _ptr(idx), _ptr(out), _ptr(lse),
+            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if pages is None:
+        _check(lib.dsa_forward(ctypes.byref(geom), *args), "dsa_forward")
+    else:
+        _check(lib.dsa_forward_paged(ctypes.byref(geom), ctypes.byref(pages), *args), "dsa_forward_paged")
     return idx, out, lse
 
 
@@ -269,16 +323,21 @@ def indexer_quantize(x, codes=None, scales=None, stream=None):
     return codes, scales
 
 
-def indexer_cache_append(geom, k_new, k_cache, k_scale_cache, stream=None):
-    """dsa_indexer_cache_append: quantise k_new [B, q_len, 128] into the caches in place."""
+def indexer_cache_append(geom, k_new, k_cache, k_scale_cache, stream=None, pages=None):
+    """dsa_indexer_cache_append (dsa_indexer_cache_append_paged when ``pages``
+    is given, with the caches the page pools): quantise k_new [B, q_len, 128]
+    into the caches in place."""
     lib = load()
     _dev(k_new, "k_new", (torch.bfloat16, torch.int16, torch.uint16, torch.float32))
     _dev(k_cache, "k_cache", (torch.uint8, _FP8))
     _dev(k_scale_cache, "k_scale_cache", (torch.float32,))
     _need(tuple(k_new.shape) == (geom.B, geom.q_len, 128), "k_new must be [B, q_len, 128]")
-    _need(tuple(k_cache.shape) == (geom.B, geom.S_max, 128), "k_cache must be [B, S_max, 128]")
-    _need(tuple(k_scale_cache.shape) == (geom.B, geom.S_max), "k_scale_cache must be [B, S_max]")
-    st = lib.dsa_indexer_cache_append(ctypes.byref(geom), _ptr(k_new), _quant_dtype(k_new), _ptr(k_cache),
-                                      _ptr(k_scale_cache), _stream(stream))
-    _check(st, "dsa_indexer_cache_append")
+    _need(tuple(k_cache.shape) == _cache_shape(geom, pages, (128,)), "k_cache shape mismatch")
+    _need(tuple(k_scale_cache.shape) == _cache_shape(geom, pages, ()), "k_scale_cache shape mismatch")
+    args = (_ptr(k_new), _quant_dtype(k_new), _ptr(k_cache), _ptr(k_scale_cache), _stream(stream))
+    if pages is None:
+        _check(lib.dsa_indexer_cache_append(ctypes.byref(geom), *args), "dsa_indexer_cache_append")
+    else:
+        _check(lib.dsa_indexer_cache_append_paged(ctypes.byref(geom), ctypes.byref(pages), *args),
+               "dsa_indexer_cache_append_paged")
     return k_cache, k_scale_cache

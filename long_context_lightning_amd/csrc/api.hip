@@ -69,6 +69,7 @@ IndexerArgs make_indexer_args(const dsa_geom* g, const void* q, const float* q_s
   a.zero_stride = 0;
   a.zero_words = 0;
   a.zero_rows = 0;
+  a.pages = PageMap{};
   return a;
 }
 
@@ -126,6 +127,27 @@ dsa_status check_mla(const dsa_geom* g, int32_t H, int32_t k, const void* q, dsa
   return DSA_ERR_UNSUPPORTED;
 }
 
+// A page table is usable with geometry g: power-of-two pages of 64..65536
+// tokens, a table wide enough for S_max tokens, pool rows addressable by int32.
+bool pages_ok(const dsa_geom* g, const dsa_pages* p) {
+  if (!p || !p->block_table || !aligned(p->block_table, 4)) return false;
+  if (p->max_pages < 1 || p->num_pages < 1) return false;
+  if (p->page_size < 64 || p->page_size > 65536 || (p->page_size & (p->page_size - 1))) return false;
+  if ((long long)p->max_pages * p->page_size < g->S_max) return false;
+  if ((long long)g->B * p->max_pages > 0x7FFFFFFFLL) return false;
+  return p->num_pages <= 0x7FFFFFFFLL / p->page_size;
+}
+
+PageMap page_map(const dsa_pages* p) {
+  PageMap m{};
+  if (!p) return m;
+  m.table = p->block_table;
+  m.max_pages = p->max_pages;
+  m.shift = __builtin_ctz((unsigned)p->page_size);
+  m.last_page = (int)(p->num_pages - 1);
+  return m;
+}
+
 MlaArgs make_mla_args(const dsa_geom* g, int32_t H, int32_t k, float sm_scale, const void* q, const void* kv,
                       const int32_t* idx, void* out, float* lse, void* ws) {
   MlaArgs a;
@@ -144,20 +166,24 @@ MlaArgs make_mla_args(const dsa_geom* g, int32_t H, int32_t k, float sm_scale, c
   a.ws = ws;
   a.row_begin = 0;
   a.row_count = (int)rows_of(g);
+  a.flat = 0;
   return a;
 }
 
 // Workspace plan of dsa_forward.
+// Paged caches always take the chunked (score buffer) path and add a buffer
+// for the translated pool rows of the selection.
 struct ForwardPlan {
   bool streaming;
   int chunk_rows;
-  size_t scores_off, topk_off, mla_off, total;
+  size_t scores_off, topk_off, mla_off, rows_off, total;
 };
 
-ForwardPlan plan_forward(int B, int q_len, int S_max, int H, int topk, dsa_dtype index_dt, dsa_dtype mla_dt) {
+ForwardPlan plan_forward(int B, int q_len, int S_max, int H, int topk, dsa_dtype index_dt, dsa_dtype mla_dt,
+                         bool paged) {
   ForwardPlan p{};
   const long long T = (long long)B * q_len;
-  p.streaming = index_dt == DSA_FP8_E4M3FN && q_len >= 64 && prefill_supported(q_len, S_max, topk);
+  p.streaming = !paged && index_dt == DSA_FP8_E4M3FN && q_len >= 64 && prefill_supported(q_len, S_max, topk);
   size_t off = 0;
   if (p.streaming) {
     p.chunk_rows = 0;
@@ -176,8 +202,141 @@ ForwardPlan plan_forward(int B, int q_len, int S_max, int H, int topk, dsa_dtype
   }
   p.mla_off = off;
   off += align_up(mla_workspace_bytes((int)T, H, topk, mla_dt == DSA_BF16));
+  p.rows_off = off;
+  if (paged) off += align_up((size_t)T * topk * sizeof(int32_t));
   p.total = off;
   return p;
+}
+
+size_t mla_paged_workspace_bytes(int T, int H, int k, dsa_dtype dt) {
+  return align_up(mla_workspace_bytes(T, H, k, dt == DSA_BF16)) + align_up((size_t)T * k * sizeof(int32_t));
+}
+
+// ---- shared bodies of the contiguous and the paged entry points (pages null = contiguous)
+
+dsa_status indexer_scores_impl(const dsa_geom* geom, const dsa_pages* pages, const void* q, dsa_dtype q_dtype,
+                               const float* q_scale, const void* w, dsa_dtype w_dtype, const void* k,
+                               dsa_dtype k_dtype, const float* k_scale, int32_t row_begin, int32_t row_count,
+                               float* scores, int64_t ld, hipStream_t stream) {
+  const dsa_status st = check_indexer_inputs(geom, q, q_dtype, q_scale, w, w_dtype, k, k_dtype, k_scale);
+  if (st != DSA_OK) return st;
+  if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
+  if (!rows_ok(geom, row_begin, row_count) || ld < geom->S_max) return DSA_ERR_INVALID_ARG;
+  if (row_count == 0) return DSA_OK;
+  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
+  IndexerArgs a = make_indexer_args(geom, q, q_scale, w, w_dtype, k, k_scale);
+  a.pages = page_map(pages);
+  a.row_begin = row_begin;
+  a.row_count = row_count;
+  a.scores = scores;
+  a.ld = ld;
+  return hip_status(run_indexer(a, q_dtype == DSA_FP8_E4M3FN, stream));
+}
+
+// The attention over translated pool rows (paged) or positions (contiguous).
+hipError_t mla_launches(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k, float sm_scale,
+                        const void* q, dsa_dtype dtype, const void* kv, const int32_t* idx, void* out, float* lse,
+                        void* mla_ws, int32_t* rows, hipStream_t stream) {
+  MlaArgs a = make_mla_args(geom, H, k, sm_scale, q, kv, idx, out, lse, mla_ws);
+  if (pages) {
+    const hipError_t e = launch_page_rows(idx, rows, (int)rows_of(geom), k, geom->q_len, geom->S_max,
+                                          geom->seq_lens, page_map(pages), stream);
+    if (e != hipSuccess) return e;
+    a.idx = rows;
+    a.flat = 1;
+  }
+  return run_mla(a, dtype == DSA_BF16, stream);
+}
+
+dsa_status sparse_mla_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k, float sm_scale,
+                           const void* q, dsa_dtype dtype, const void* kv, const int32_t* idx, void* out,
+                           float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const dsa_status st = check_mla(geom, H, k, q, dtype, kv, idx, out, lse);
+  if (st != DSA_OK) return st;
+  if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
+  const int T = (int)rows_of(geom);
+  const size_t mla_bytes = mla_workspace_bytes(T, H, k, dtype == DSA_BF16);
+  const size_t need = pages ? mla_paged_workspace_bytes(T, H, k, dtype) : mla_bytes;
+  if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
+  int32_t* rows = pages ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align_up(mla_bytes)) : nullptr;
+  return hip_status(mla_launches(geom, pages, H, k, sm_scale, q, dtype, kv, idx, out, lse, ws, rows, stream));
+}
+
+dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H, float sm_scale,
+                        const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                        const void* index_w, dsa_dtype index_w_dtype, const void* index_k,
+                        const float* index_k_scale, const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype,
+                        int32_t* idx_out, void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  dsa_status st = check_indexer_inputs(geom, index_q, index_dtype, index_q_scale, index_w, index_w_dtype, index_k,
+                                       index_dtype, index_k_scale);
+  if (st != DSA_OK) return st;
+  if (!idx_out || !aligned(idx_out, 4) || topk < 1) return DSA_ERR_INVALID_ARG;
+  st = check_mla(geom, H, topk, mla_q, mla_dtype, mla_kv, idx_out, out, lse);
+  if (st != DSA_OK) return st;
+  if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
+  const ForwardPlan p =
+      plan_forward(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype, pages != nullptr);
+  if (!p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+  const int T = (int)rows_of(geom);
+  IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
+  ia.pages = page_map(pages);
+  hipError_t e = hipSuccess;
+  if (p.streaming) {
+    ia.row_begin = 0;
+    ia.row_count = T;
+    e = launch_indexer_topk_prefill(ia, topk, idx_out, wsb, stream);
+  } else {
+    float* scores = reinterpret_cast<float*>(wsb + p.scores_off);
+    const bool fp8 = index_dtype == DSA_FP8_E4M3FN;
+    for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
+      const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
+      TopkArgs ta;
+      ta.B = geom->B;
+      ta.q_len = geom->q_len;
+      ta.S_max = geom->S_max;
+      ta.seq_lens = geom->seq_lens;
+      ta.scores = scores;
+      ta.ld = geom->S_max;
+      ta.row_begin = r0;
+      ta.row_count = rc;
+      ta.k = topk;
+      ta.idx = idx_out + (long long)r0 * topk;
+      ta.ws = wsb + p.topk_off;
+      ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
+      ia.row_begin = r0;
+      ia.row_count = rc;
+      ia.scores = scores;
+      ia.ld = geom->S_max;
+      topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
+      ia.zero_rows = rc;
+      e = run_indexer(ia, fp8, stream);
+      if (e != hipSuccess) break;
+      e = run_topk(ta, stream);
+    }
+  }
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  return hip_status(mla_launches(geom, pages, H, topk, sm_scale, mla_q, mla_dtype, mla_kv, idx_out, out, lse,
+                                 wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream));
+}
+
+dsa_status cache_append_impl(const dsa_geom* geom, const dsa_pages* pages, const void* k_new, dsa_dtype k_dtype,
+                             uint8_t* k_cache, float* k_scale_cache, hipStream_t stream) {
+  if (!geom_ok(geom) || !k_new || !k_cache || !k_scale_cache) return DSA_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(k_cache, 4) || !aligned(k_scale_cache, 4)) return DSA_ERR_INVALID_ARG;
+  if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
+  if (k_dtype != DSA_BF16 && k_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  QuantArgs a{};
+  a.x = k_new;
+  a.rows = rows_of(geom);
+  a.codes = k_cache;
+  a.scales = k_scale_cache;
+  a.seq_lens = geom->seq_lens;
+  a.q_len = geom->q_len;
+  a.S_max = geom->S_max;
+  a.pages = page_map(pages);
+  return hip_status(launch_cache_append(a, k_dtype == DSA_BF16, stream));
 }
 
 }  // namespace
@@ -188,17 +347,17 @@ dsa_status dsa_indexer_scores(const dsa_geom* geom, const void* q, dsa_dtype q_d
                               const void* w, dsa_dtype w_dtype, const void* k, dsa_dtype k_dtype,
                               const float* k_scale, int32_t row_begin, int32_t row_count, float* scores,
                               int64_t ld, hipStream_t stream) {
-  const dsa_status st = check_indexer_inputs(geom, q, q_dtype, q_scale, w, w_dtype, k, k_dtype, k_scale);
-  if (st != DSA_OK) return st;
-  if (!rows_ok(geom, row_begin, row_count) || ld < geom->S_max) return DSA_ERR_INVALID_ARG;
-  if (row_count == 0) return DSA_OK;
-  if (!scores || !aligned(scores, 4)) return DSA_ERR_INVALID_ARG;
-  IndexerArgs a = make_indexer_args(geom, q, q_scale, w, w_dtype, k, k_scale);
-  a.row_begin = row_begin;
-  a.row_count = row_count;
-  a.scores = scores;
-  a.ld = ld;
-  return hip_status(run_indexer(a, q_dtype == DSA_FP8_E4M3FN, stream));
+  return indexer_scores_impl(geom, nullptr, q, q_dtype, q_scale, w, w_dtype, k, k_dtype, k_scale, row_begin,
+                             row_count, scores, ld, stream);
+}
+
+dsa_status dsa_indexer_scores_paged(const dsa_geom* geom, const dsa_pages* pages, const void* q, dsa_dtype q_dtype,
+                                    const float* q_scale, const void* w, dsa_dtype w_dtype, const void* k_pool,
+                                    dsa_dtype k_dtype, const float* k_scale_pool, int32_t row_begin,
+                                    int32_t row_count, float* scores, int64_t ld, hipStream_t stream) {
+  if (!pages) return DSA_ERR_INVALID_ARG;
+  return indexer_scores_impl(geom, pages, q, q_dtype, q_scale, w, w_dtype, k_pool, k_dtype, k_scale_pool,
+                             row_begin, row_count, scores, ld, stream);
 }
 
 size_t dsa_topk_workspace_size(int32_t row_count, int32_t S_max, int32_t k) {
@@ -240,18 +399,31 @@ size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_
 dsa_status dsa_sparse_mla(const dsa_geom* geom, int32_t H, int32_t k, float sm_scale, const void* q,
                           dsa_dtype dtype, const void* kv, const int32_t* idx, void* out, float* lse, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
-  const dsa_status st = check_mla(geom, H, k, q, dtype, kv, idx, out, lse);
-  if (st != DSA_OK) return st;
-  const size_t need = dsa_sparse_mla_workspace_size(geom->B, geom->q_len, H, k, dtype);
-  if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
-  const MlaArgs a = make_mla_args(geom, H, k, sm_scale, q, kv, idx, out, lse, ws);
-  return hip_status(run_mla(a, dtype == DSA_BF16, stream));
+  return sparse_mla_impl(geom, nullptr, H, k, sm_scale, q, dtype, kv, idx, out, lse, ws, ws_bytes, stream);
+}
+
+size_t dsa_sparse_mla_paged_workspace_size(int32_t B, int32_t q_len, int32_t H, int32_t k, dsa_dtype dtype) {
+  if (B < 1 || q_len < 1 || H < 1 || k < 1) return 0;
+  return mla_paged_workspace_bytes(B * q_len, H, k, dtype);
+}
+
+dsa_status dsa_sparse_mla_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k, float sm_scale,
+                                const void* q, dsa_dtype dtype, const void* kv_pool, const int32_t* idx, void* out,
+                                float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!pages) return DSA_ERR_INVALID_ARG;
+  return sparse_mla_impl(geom, pages, H, k, sm_scale, q, dtype, kv_pool, idx, out, lse, ws, ws_bytes, stream);
 }
 
 size_t dsa_forward_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t topk,
                                   dsa_dtype index_dtype, dsa_dtype mla_dtype) {
   if (B < 1 || q_len < 1 || S_max < 1 || H < 1 || topk < 1) return 0;
-  return plan_forward(B, q_len, S_max, H, topk, index_dtype, mla_dtype).total;
+  return plan_forward(B, q_len, S_max, H, topk, index_dtype, mla_dtype, false).total;
+}
+
+size_t dsa_forward_paged_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t topk,
+                                        dsa_dtype index_dtype, dsa_dtype mla_dtype) {
+  if (B < 1 || q_len < 1 || S_max < 1 || H < 1 || topk < 1) return 0;
+  return plan_forward(B, q_len, S_max, H, topk, index_dtype, mla_dtype, true).total;
 }
 
 dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale, const void* index_q,
@@ -259,55 +431,20 @@ dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_s
                        dsa_dtype index_w_dtype, const void* index_k, const float* index_k_scale,
                        const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype, int32_t* idx_out, void* out,
                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  dsa_status st = check_indexer_inputs(geom, index_q, index_dtype, index_q_scale, index_w, index_w_dtype, index_k,
-                                       index_dtype, index_k_scale);
-  if (st != DSA_OK) return st;
-  if (!idx_out || !aligned(idx_out, 4) || topk < 1) return DSA_ERR_INVALID_ARG;
-  st = check_mla(geom, H, topk, mla_q, mla_dtype, mla_kv, idx_out, out, lse);
-  if (st != DSA_OK) return st;
-  const ForwardPlan p = plan_forward(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype);
-  if (!p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
-  if (ws_bytes < p.total || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
-  char* wsb = static_cast<char*>(ws);
-  const int T = (int)rows_of(geom);
-  IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
-  hipError_t e = hipSuccess;
-  if (p.streaming) {
-    ia.row_begin = 0;
-    ia.row_count = T;
-    e = launch_indexer_topk_prefill(ia, topk, idx_out, wsb, stream);
-  } else {
-    float* scores = reinterpret_cast<float*>(wsb + p.scores_off);
-    const bool fp8 = index_dtype == DSA_FP8_E4M3FN;
-    for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
-      const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
-      TopkArgs ta;
-      ta.B = geom->B;
-      ta.q_len = geom->q_len;
-      ta.S_max = geom->S_max;
-      ta.seq_lens = geom->seq_lens;
-      ta.scores = scores;
-      ta.ld = geom->S_max;
-      ta.row_begin = r0;
-      ta.row_count = rc;
-      ta.k = topk;
-      ta.idx = idx_out + (long long)r0 * topk;
-      ta.ws = wsb + p.topk_off;
-      ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
-      ia.row_begin = r0;
-      ia.row_count = rc;
-      ia.scores = scores;
-      ia.ld = geom->S_max;
-      topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
-      ia.zero_rows = rc;
-      e = run_indexer(ia, fp8, stream);
-      if (e != hipSuccess) break;
-      e = run_topk(ta, stream);
-    }
-  }
-  if (e != hipSuccess) return DSA_ERR_HIP;
-  const MlaArgs ma = make_mla_args(geom, H, topk, sm_scale, mla_q, mla_kv, idx_out, out, lse, wsb + p.mla_off);
-  return hip_status(run_mla(ma, mla_dtype == DSA_BF16, stream));
+  return forward_impl(geom, nullptr, topk, H, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                      index_k, index_k_scale, mla_q, mla_kv, mla_dtype, idx_out, out, lse, ws, ws_bytes, stream);
+}
+
+dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H, float sm_scale,
+                             const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                             const void* index_w, dsa_dtype index_w_dtype, const void* index_k_pool,
+                             const float* index_k_scale_pool, const void* mla_q, const void* mla_kv_pool,
+                             dsa_dtype mla_dtype, int32_t* idx_out, void* out, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  if (!pages) return DSA_ERR_INVALID_ARG;
+  return forward_impl(geom, pages, topk, H, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                      index_k_pool, index_k_scale_pool, mla_q, mla_kv_pool, mla_dtype, idx_out, out, lse, ws,
+                      ws_bytes, stream);
 }
 
 dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_t rows, uint8_t* codes, float* scales,
@@ -327,18 +464,14 @@ dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_t rows, 
 
 dsa_status dsa_indexer_cache_append(const dsa_geom* geom, const void* k_new, dsa_dtype k_dtype, uint8_t* k_cache,
                                     float* k_scale_cache, hipStream_t stream) {
-  if (!geom_ok(geom) || !k_new || !k_cache || !k_scale_cache) return DSA_ERR_INVALID_ARG;
-  if (!aligned(k_new, 16) || !aligned(k_cache, 4) || !aligned(k_scale_cache, 4)) return DSA_ERR_INVALID_ARG;
-  if (k_dtype != DSA_BF16 && k_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
-  QuantArgs a{};
-  a.x = k_new;
-  a.rows = rows_of(geom);
-  a.codes = k_cache;
-  a.scales = k_scale_cache;
-  a.seq_lens = geom->seq_lens;
-  a.q_len = geom->q_len;
-  a.S_max = geom->S_max;
-  return hip_status(launch_cache_append(a, k_dtype == DSA_BF16, stream));
+  return cache_append_impl(geom, nullptr, k_new, k_dtype, k_cache, k_scale_cache, stream);
+}
+
+dsa_status dsa_indexer_cache_append_paged(const dsa_geom* geom, const dsa_pages* pages, const void* k_new,
+                                          dsa_dtype k_dtype, uint8_t* k_pool, float* k_scale_pool,
+                                          hipStream_t stream) {
+  if (!pages) return DSA_ERR_INVALID_ARG;
+  return cache_append_impl(geom, pages, k_new, k_dtype, k_pool, k_scale_pool, stream);
 }
 
 const char* dsa_status_string(dsa_status s) {

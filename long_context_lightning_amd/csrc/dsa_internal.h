@@ -29,6 +29,24 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Paged cache addressing: token s of sequence b lives in row s % P of page
+// table[b * max_pages + s / P] of a pool of num_pages pages (P = 1 << shift
+// tokens each).  Page ids are clamped into the pool, so a bad table entry
+// reads or writes a wrong page of the pool, never memory outside it.  A null
+// table means contiguous caches [B, S_max, ...].
+struct PageMap {
+  const int32_t* table;
+  int max_pages, shift, last_page;  // last_page = num_pages - 1
+  __device__ __forceinline__ int page(int b, int j) const {
+    const int p = table[(long long)b * max_pages + j];
+    return p < 0 ? 0 : (p > last_page ? last_page : p);
+  }
+  // pool row of token s of sequence b
+  __device__ __forceinline__ int row(int b, int s) const {
+    return (page(b, s >> shift) << shift) | (s & ((1 << shift) - 1));
+  }
+};
+
 // Length of sequence b clamped into [0, S_max].
 __device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int S_max) {
   int L = seq_lens[b];
@@ -184,6 +202,7 @@ struct IndexerArgs {
   uint32_t* zero_base;
   long long zero_stride;
   int zero_words, zero_rows;
+  PageMap pages;          // k / k_scale are page pools when pages.table is set
 };
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t s);
@@ -210,6 +229,7 @@ struct QuantArgs {
   float* scales;            // [rows], or the scale cache [B, S_max]
   const int32_t* seq_lens;  // cache append only
   int q_len, S_max;         // cache append only
+  PageMap pages;            // cache append into page pools when pages.table is set
 };
 hipError_t launch_quantize(const QuantArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_cache_append(const QuantArgs& a, bool bf16, hipStream_t s);
@@ -230,7 +250,16 @@ struct MlaArgs {
   float* lse;             // [T,H] or null
   void* ws;
   int row_begin, row_count;  // rows handled by this launch
+  // idx holds rows of a flat pool (kv [rows, 576]) rather than positions of
+  // sequence b: an entry is valid iff it is >= 0 (the causal bound was applied
+  // when the positions were translated).
+  int flat;
 };
+
+// Positions idx[t, m] -> pool rows of the paged cache (-1 where the position
+// is invalid for row t: negative or past its query position).
+hipError_t launch_page_rows(const int32_t* idx, int32_t* rows, int T, int k, int q_len, int S_max,
+                            const int32_t* seq_lens, const PageMap& pages, hipStream_t s);
 
 size_t mla_workspace_bytes(int T, int H, int k, int is_bf16);
 hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t s);

@@ -69,7 +69,7 @@ __device__ __forceinline__ void zero_side_job(const IndexerArgs& a) {
   }
 }
 
-template <int NQ, bool WBF16>
+template <int NQ, bool WBF16, bool PAGED>
 __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
   zero_side_job(a);
   const int lane = threadIdx.x & 63;
@@ -97,21 +97,44 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
   if (kend <= chunk0) return;
   const int nsteps = (kend - chunk0 + kKeysPerBlock - 1) / kKeysPerBlock;
 
-  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (size_t)rg.b * a.S_max * kDI;
-  const float* ksb = a.k_scale ? a.k_scale + (size_t)rg.b * a.S_max : nullptr;
+  const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (PAGED ? 0 : (size_t)rg.b * a.S_max * kDI);
+  const float* ksb = a.k_scale ? a.k_scale + (PAGED ? 0 : (size_t)rg.b * a.S_max) : nullptr;
+  // Paged caches: a page holds a power of two >= 64 tokens, so the 64 keys
+  // of one wave step never straddle a page, and a 4096-key chunk touches at
+  // most 64 pages.  Lane i holds the id of the chunk's i-th page (read once),
+  // and each step takes its page from the lane by a readlane: no table read
+  // sits in front of a key load.
+  int page_j0 = 0, lane_page = 0;
+  if constexpr (PAGED) {
+    page_j0 = chunk0 >> a.pages.shift;
+    const int np = ((kend - 1) >> a.pages.shift) - page_j0 + 1;
+    lane_page = a.pages.page(rg.b, page_j0 + min(lane, np - 1));
+  }
   // Every key load is issued unconditionally (addresses clamped into
   // [chunk0, kend), a missing k-scale read from a unit constant), so the
   // compiler's memory-counter waits stay exact: the next step's keys stay in
   // flight while the current step computes.
   auto load_keys = [&](int step, v8i (&kf)[4], float& ks) {
     const int kw = chunk0 + step * kKeysPerBlock + wave * kKeysPerWave;
+    const uint8_t* kwin = kb;
+    const float* kswin = ksb;
+    if constexpr (PAGED) {
+      // the step's keys (clamped like the loads) lie in the 64-key window wb,
+      // whose tokens are pool rows s + shift_rows
+      const int wb = min(kw, kend - 1) & ~(kKeysPerWave - 1);
+      const int pg = __builtin_amdgcn_readlane(lane_page, (wb >> a.pages.shift) - page_j0);
+      const long long shift_rows =
+          ((long long)pg << a.pages.shift) + (wb & ((1 << a.pages.shift) - 1)) - wb;
+      kwin = kb + shift_rows * kDI;
+      kswin = ksb ? ksb + shift_rows : nullptr;
+    }
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       const int s = min(kw + 16 * blk + c, kend - 1);  // keys past kend are never stored
-      kf[blk] = load32(kb + (size_t)s * kDI + 32 * g);
+      kf[blk] = load32(kwin + (size_t)s * kDI + 32 * g);
     }
     const int s_l = min(kw + lane, kend - 1);
-    ks = *(ksb ? ksb + s_l : &g_unit_scale);
+    ks = *(kswin ? kswin + s_l : &g_unit_scale);
   };
   v8i kf_a[4], kf_b[4];
   float ks_a, ks_b;
@@ -227,7 +250,8 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
     out[s] = -INFINITY;
     return;
   }
-  const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + ((size_t)b * a.S_max + s) * kDI);
+  const size_t krow = a.pages.table ? (size_t)a.pages.row(b, s) : (size_t)b * a.S_max + s;
+  const float4* kr = reinterpret_cast<const float4*>(static_cast<const float*>(a.k) + krow * kDI);
   float kreg[kDI];
 #pragma unroll
   for (int d = 0; d < kDI / 4; ++d) {
@@ -241,7 +265,7 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
     for (int d = 0; d < kDI; ++d) dot = fmaf(qs[j * kDI + d], kreg[d], dot);
     score = fmaf(wsh[j], fmaxf(dot, 0.f), score);
   }
-  const float ksc = a.k_scale ? a.k_scale[(size_t)b * a.S_max + s] : 1.0f;
+  const float ksc = a.k_scale ? a.k_scale[krow] : 1.0f;
   out[s] = score * ksc;
 }
 
@@ -249,7 +273,8 @@ __global__ __launch_bounds__(256) void k_indexer_f32(IndexerArgs a) {
 
 template <int NQ, bool WBF16>
 static void launch_fp8_variant(const IndexerArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16>), grid, dim3(256), 0, stream, a);
+  if (a.pages.table) hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, true>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((k_indexer_fp8<NQ, WBF16, false>), grid, dim3(256), 0, stream, a);
 }
 
 hipError_t launch_indexer_fp8(const IndexerArgs& a, hipStream_t stream) {

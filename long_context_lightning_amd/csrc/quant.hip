@@ -89,10 +89,11 @@ __global__ __launch_bounds__(kThreads) void k_quant(QuantArgs a) {
       long long dst = blk;
       if (APPEND) {
         // row b*q_len + i -> position clamp(seq_lens[b], 0, S_max) - q_len + i
+        // (a pool row when the cache is paged)
         const int b = (int)(blk / a.q_len), i = (int)(blk - (long long)b * a.q_len);
         const int s = clamped_len(a.seq_lens, b, a.S_max) - a.q_len + i;
         if (s < 0) continue;
-        dst = (long long)b * a.S_max + s;
+        dst = a.pages.table ? (long long)a.pages.row(b, s) : (long long)b * a.S_max + s;
       }
       reinterpret_cast<uint32_t*>(a.codes + dst * kBlock)[j] = packed;
       if (j == 0) a.scales[dst] = scale;

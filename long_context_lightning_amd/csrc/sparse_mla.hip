@@ -267,10 +267,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   asm volatile("" : "+v"(aoff), "+v"(roff0), "+v"(roff1), "+v"(voff), "+v"(poff));
 
   TileSrc src;
-  src.kvb = static_cast<const uint16_t*>(a.kv) + (size_t)b * a.S_max * kDQK;
+  src.kvb = static_cast<const uint16_t*>(a.kv) + (a.flat ? 0 : (size_t)b * a.S_max * kDQK);
   src.idx_row = idx + (size_t)t * a.k;
   src.m1 = m1;
-  src.pos = pos;
+  src.pos = a.flat ? 0x7FFFFFFF : pos;  // flat pool rows: the causal bound is already applied
   unsigned char* const vmb = reinterpret_cast<unsigned char*>(vmask);
   const uint32_t ring_off = lds_offset(ring);
 
@@ -640,13 +640,14 @@ __global__ __launch_bounds__(256) void k_mla_f32(MlaArgs a) {
   const float* qrow = static_cast<const float*>(a.q) + ((size_t)t * a.H + h) * kDQK;
   for (int d = tid; d < kDQK; d += 256) qs[d] = qrow[d];
   __syncthreads();
-  const float* kvb = static_cast<const float*>(a.kv) + (size_t)b * a.S_max * kDQK;
+  const float* kvb = static_cast<const float*>(a.kv) + (a.flat ? 0 : (size_t)b * a.S_max * kDQK);
   const int32_t* idx_row = a.idx + (size_t)t * a.k;
+  const int smax = a.flat ? 0x7FFFFFFF : pos;  // flat pool rows: the causal bound is already applied
   float lmax = -INFINITY;
   for (int m = tid; m < a.k; m += 256) {
     const int s = idx_row[m];
     float z = -INFINITY;
-    if (s >= 0 && s <= pos) {
+    if (s >= 0 && s <= smax && pos >= 0) {
       const float* kr = kvb + (size_t)s * kDQK;
       float dot = 0.f;
       for (int d = 0; d < kDQK; ++d) dot = fmaf(qs[d], kr[d], dot);

@@ -3,10 +3,12 @@
 Shared by the GPU tests, ``bench.py`` and the oracle tests.  This package
 holds input generation only (random draws, the storage encoders that turn
 them into fp8 / bf16 bit patterns, the planted and tied structures of the
-workloads); none of the indexer, top-k or attention arithmetic lives here.
+workloads, the block tables of paged caches); none of the indexer, top-k or
+attention arithmetic lives here.
 """
 
 from .encode import encode_bf16_rne, encode_e4m3fn_rne, quantize_per_token
+from .pages import make_block_table, share_prefix
 from .workloads import Workload, make_workload, standard_workload, WORKLOAD_NAMES
 
 __all__ = [
@@ -17,4 +19,6 @@ __all__ = [
     "make_workload",
     "standard_workload",
     "WORKLOAD_NAMES",
+    "make_block_table",
+    "share_prefix",
 ]

@@ -115,3 +115,55 @@ def test_quantize_and_cache_append_validation():
     assert lib.dsa_indexer_cache_append(ctypes.byref(g), P(FAKE), 1, None, P(FAKE), None) == 1
     bad = _geom(B=1, q_len=20, S=16)
     assert lib.dsa_indexer_cache_append(ctypes.byref(bad), P(FAKE), 1, P(FAKE), P(FAKE), None) == 1
+
+
+def _pages(max_pages=1, page_size=64, num_pages=4, table=FAKE):
+    return lcl.Pages(table, max_pages, page_size, num_pages)
+
+
+def test_paged_validation():
+    """Page tables are checked on the host: null or misaligned table, a page
+    size that is not a power of two in [64, 65536], a table too narrow for
+    S_max, a pool too large for int32 rows."""
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=1, S=256)
+
+    def scores(pg):
+        return lib.dsa_indexer_scores_paged(ctypes.byref(g), pg, P(FAKE), 2, None, P(FAKE), 1, P(FAKE), 2, None,
+                                            0, 0, P(FAKE), 256, None)
+    assert scores(None) == 1
+    assert scores(ctypes.byref(_pages(max_pages=4))) == 0                        # valid, nothing to do
+    assert scores(ctypes.byref(_pages(max_pages=4, table=0))) == 1              # null table
+    assert scores(ctypes.byref(_pages(max_pages=4, table=FAKE + 2))) == 1       # misaligned table
+    assert scores(ctypes.byref(_pages(max_pages=3))) == 1                       # 3 * 64 < S_max
+    assert scores(ctypes.byref(_pages(max_pages=8, page_size=32))) == 1         # page below 64
+    assert scores(ctypes.byref(_pages(max_pages=4, page_size=96))) == 1         # not a power of two
+    assert scores(ctypes.byref(_pages(max_pages=1, page_size=1 << 17))) == 1    # page above 65536
+    assert scores(ctypes.byref(_pages(max_pages=4, num_pages=0))) == 1
+    assert scores(ctypes.byref(_pages(max_pages=4, num_pages=1 << 25))) == 1    # pool rows past int32
+    assert scores(ctypes.byref(_pages(max_pages=4, num_pages=(1 << 25) - 1))) == 0
+
+    ok = ctypes.byref(_pages(max_pages=4))
+    need = lib.dsa_sparse_mla_paged_workspace_size(2, 1, 128, 2048, 1)
+    assert need >= 2 * 2048 * 4                                                 # the translated rows
+    mla = lambda pg, wsb: lib.dsa_sparse_mla_paged(ctypes.byref(g), pg, 128, 2048, 0.1, P(FAKE), 1, P(FAKE),
+                                                   P(FAKE), P(FAKE), None, P(FAKE), wsb, None)
+    assert mla(None, need) == 1
+    assert mla(ctypes.byref(_pages(max_pages=2)), need) == 1
+    assert mla(ok, need - 1) == 3
+
+    fneed = lib.dsa_forward_paged_workspace_size(2, 1, 256, 128, 2048, 2, 1)
+    assert fneed > lib.dsa_forward_workspace_size(2, 1, 256, 128, 2048, 2, 1)
+    fwd = lambda pg, wsb: lib.dsa_forward_paged(ctypes.byref(g), pg, 2048, 128, 0.1, P(FAKE), 2, None, P(FAKE), 1,
+                                                P(FAKE), None, P(FAKE), P(FAKE), 1, P(FAKE), P(FAKE), None, P(FAKE),
+                                                wsb, None)
+    assert fwd(None, fneed) == 1
+    assert fwd(ok, fneed - 1) == 3
+    # a long prefill is never streamed when paged: the workspace holds the score chunk
+    pre = lib.dsa_forward_paged_workspace_size(1, 65536, 65536, 128, 2048, 2, 1)
+    assert pre >= (256 << 20) + 65536 * 2048 * 4                               # score chunk + translated rows
+
+    app = lambda pg: lib.dsa_indexer_cache_append_paged(ctypes.byref(g), pg, P(FAKE), 1, P(FAKE), P(FAKE), None)
+    assert app(None) == 1
+    assert app(ctypes.byref(_pages(max_pages=4, page_size=100))) == 1
