@@ -191,6 +191,9 @@ def main():
                 "traffic": measured_traffic("indexer_fp8_decode128k")}
     del scores
 
+    # ------------------------------------------- paged caches, same decode
+    paged = bench_paged(args, lcl, torch, np, dev, stream, evict, wl, d, geom, idx, out, lse, ms)
+
     # ------------------------------------------- fp8 quantisation / append
     quant = bench_quant(lcl, torch, dev, stream, evict, wl)
 
@@ -226,10 +229,74 @@ def main():
         "roofline": roofline,
         "stages": stages,
         "quantize": quant,
+        "paged": paged,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_paged(args, lcl, torch, np, dev, stream, evict, wl, d, geom, idx, out, lse, contiguous_ms):
+    """The same 128K decode step on paged caches (dsa_forward_paged): the
+    three caches copied into pools of 64-token pages in the scattered order of
+    a seeded block table, timed like the contiguous step (LLC eviction before
+    each step, event pair around it), plus its two paged stages alone."""
+    from synth import make_block_table
+    P = 64
+    _, clean, num_pages = make_block_table(10, wl.B, wl.seq_lens, wl.S_max, P)
+    table = torch.from_numpy(clean).to(dev)
+    dst = torch.from_numpy(clean.reshape(-1).astype(np.int64)).to(dev)
+
+    def pool(c, tail):
+        p = torch.zeros((num_pages, P) + tail, dtype=c.dtype, device=dev)
+        return p.index_copy_(0, dst, c.reshape((-1, P) + tail))
+
+    ki_pool, ks_pool, kv_pool = pool(d["ki"], (128,)), pool(d["ks"], ()), pool(d["kv"], (576,))
+    pages = lcl.make_pages(table, P, num_pages)
+    T, k, H = wl.T, wl.topk, wl.H
+    ws = torch.empty(lcl.forward_paged_workspace_size(wl.B, wl.q_len, wl.S_max, H, k, lcl.FP8_E4M3FN, lcl.BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def forward():
+        lcl.forward(geom, k, wl.sm_scale, d["qi"], d["w"], ki_pool, d["qm"], kv_pool, index_k_scale=ks_pool,
+                    idx=idx, out=out, lse=lse, ws=ws, pages=pages)
+
+    for _ in range(args.warmup):
+        evict()
+        forward()
+    torch.cuda.synchronize()
+    scores = torch.empty((T, wl.S_max), dtype=torch.float32, device=dev)
+    mla_ws = torch.empty(max(lcl.sparse_mla_paged_workspace_size(wl.B, wl.q_len, H, k, lcl.BF16), 256),
+                         dtype=torch.uint8, device=dev)
+    st = {n: [] for n in ("forward", "indexer", "sparse_mla")}
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        evict()
+        e[0].record(stream)
+        forward()
+        e[1].record(stream)
+        evict()
+        e[2].record(stream)
+        lcl.indexer_scores(geom, d["qi"], d["w"], ki_pool, k_scale=ks_pool, scores=scores, pages=pages)
+        e[3].record(stream)
+        evict()
+        e[4].record(stream)
+        lcl.sparse_mla(geom, d["qm"], kv_pool, idx, wl.sm_scale, out=out, lse=lse, ws=mla_ws, pages=pages)
+        e[5].record(stream)
+        torch.cuda.synchronize()
+        st["forward"].append(e[0].elapsed_time(e[1]))
+        st["indexer"].append(e[2].elapsed_time(e[3]))
+        st["sparse_mla"].append(e[4].elapsed_time(e[5]))
+    us = {n: sum(v) / len(v) * 1e3 for n, v in st.items()}
+    qps = T / (us["forward"] * 1e-6)
+    log(f"paged decode (64-token pages): {us['forward']:.1f} us/step -> {qps:,.0f} queries/s "
+        f"({us['forward'] / (contiguous_ms * 1e3):.3f}x the contiguous step); indexer {us['indexer']:.1f} us, "
+        f"sparse MLA incl. page-row translation {us['sparse_mla']:.1f} us")
+    del ki_pool, ks_pool, kv_pool, ws, scores, mla_ws
+    torch.cuda.empty_cache()
+    return {"page_size": P, "num_pages": int(num_pages), "us_per_step": round(us["forward"], 2),
+            "queries_per_s": round(qps, 1), "vs_contiguous_step": round(us["forward"] / (contiguous_ms * 1e3), 4),
+            "indexer_us": round(us["indexer"], 2), "sparse_mla_us": round(us["sparse_mla"], 2)}
 
 
 def bench_quant(lcl, torch, dev, stream, evict, wl):
