@@ -22,6 +22,10 @@ the passage of the pages it follows:
 * ``quant``: the ``act_quant`` step of the ``Indexer`` code block (per-128
   block e4m3fn codes with an ``amax / 448`` scale) and the key-cache append
   ``k_cache[:bsz, start_pos:end_pos] = k_fp8``.
+* ``mha``: MHA-mode prefill for sequences no longer than top-k ("详解DSA",
+  "DSA计算流" and its MLA forward code block; the charlestar page's
+  short-prompt paragraph): ``wkv_b`` decompression, causal attention over the
+  per-head keys and values.
 * ``paged``: paged caches (charlestar page, "Prefill 与 decode 中发生了什么"
   and "Top-k 是算法与 kernel 的交界面"): a block table maps a logical
   position to a page and an offset.
@@ -31,6 +35,7 @@ the passage of the pages it follows:
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_times_512
 from .quant import cache_append, e4m3fn_nearest, quantize_blocks
 from .paged import gather_pages, scatter_pages
+from .mha import decompress as mha_decompress, mha_prefill
 from .dsa import (
     query_positions,
     indexer_scores,
@@ -53,4 +58,6 @@ __all__ = [
     "cache_append",
     "gather_pages",
     "scatter_pages",
+    "mha_decompress",
+    "mha_prefill",
 ]

@@ -13,7 +13,8 @@ Recipe (values are generated in float32 / float64 on the host, then encoded):
 
 * fp8 configs: indexer q = e4m3fn(N(0,1)) with no scale; indexer k =
   per-token quantised N(0,1) (e4m3fn codes + fp32 scale amax/448); head
-  weights w = bf16(N(0,1)/8); MLA q and latent cache = bf16(N(0,1)).
+  weights w = bf16(N(0,1)/8); MLA q and latent cache = bf16(N(0,1)); for
+  MHA mode, q = bf16(N(0,1)) [T, H, 192] and wkv_b = bf16(N(0,1)/sqrt(512)).
 * fp32 config ("tiny"): indexer q, k ~ N(0,1)/sqrt(128), w ~ N(0,1), MLA q
   and latent cache ~ N(0,1), all float32, no scales.
 * ``plant``: one template (q*, w*) is drawn; the planted query rows get
@@ -37,7 +38,8 @@ HI, DI, DQK, DV = 64, 128, 576, 512
 ROW_BLOCK = 64
 POS_BLOCK = 4096
 
-_STREAM = {"qi": 1, "w": 2, "ki": 3, "qm": 4, "kv": 5, "plant": 6, "pool": 7}
+_STREAM = {"qi": 1, "w": 2, "ki": 3, "qm": 4, "kv": 5, "plant": 6, "pool": 7, "qh": 8, "wkvb": 9}
+D_QH, D_NOPE_V = 192, 256   # MHA mode: q = [nope 128 | rope 64]; wkv_b rows per head = [k_nope 128 | v 128]
 
 
 def _rng(*key):
@@ -188,6 +190,22 @@ class Workload:
             return self._by_blocks(rows, "qm", mk, (self.H, DQK), np.uint16)
         mk = lambda g, n: _normal32(g, (n, self.H, DQK))
         return self._by_blocks(rows, "qm", mk, (self.H, DQK), np.float32)
+
+    def qh(self, rows=None):
+        """MHA-mode queries [R, H, 192] (nope | rope): bf16 bits or float32."""
+        if self.fp8:
+            mk = lambda g, n: encode_bf16_rne(_normal32(g, (n, self.H, D_QH)))
+            return self._by_blocks(rows, "qh", mk, (self.H, D_QH), np.uint16)
+        mk = lambda g, n: _normal32(g, (n, self.H, D_QH))
+        return self._by_blocks(rows, "qh", mk, (self.H, D_QH), np.float32)
+
+    def wkv_b(self):
+        """Latent up-projection [H, 256, 512] (per head: k_nope rows, then v
+        rows), N(0, 1/512) so decompressed keys and values are ~N(0, 1):
+        bf16 bits or float32."""
+        g = _rng(self.seed, _STREAM["wkvb"])
+        w = _normal32(g, (self.H, D_NOPE_V, DQK - 64)) / np.float32(math.sqrt(DQK - 64))
+        return encode_bf16_rne(w) if self.fp8 else w
 
     def _apply_plant(self, rows, out, what):
         p = self._planted()
