@@ -283,6 +283,34 @@ DSA_API dsa_status dsa_indexer_cache_append_paged(const dsa_geom* geom, const ds
                                     const void* k_new, dsa_dtype k_dtype,
                                     uint8_t* k_pool, float* k_scale_pool, hipStream_t stream);
 
+/* MHA-mode prefill for sequences no longer than top-k ("详解DSA", section
+ * "DSA计算流 & 性能分析": prefill inside top-k runs in MHA mode, and a
+ * sequence no longer than top-k keeps every position so the indexer can be
+ * skipped; the MHA branch of the MLA forward code block on that page; the
+ * charlestar page's short-prompt paragraph: a masked MHA stands in for DSA
+ * when L <= k).  The latent rows are decompressed per head through wkv_b,
+ *   [k_nope | v][b, s, h] = wkv_b[h] . kv[b, s, 0:512]      (128 + 128 dims)
+ * and every query attends causally to all keys up to its position:
+ *   k_s      = [k_nope[b,s,h] (128) | kv[b, s, 512:576] (64, shared)]
+ *   z_s      = sm_scale * q[t, h, :] . k_s                    for s <= pos(t)
+ *   out[t,h] = sum_s softmax(z)_s * v[b, s, h]     lse[t,h] = log sum_s exp(z_s)
+ * This equals the DSA forward (MQA mode, dsa_forward) with weights absorbed
+ * whenever every seq_lens[b] <= topk, the case it is meant for: there the
+ * top-k keeps every position.  Longer sequences get dense causal attention,
+ * not DSA.
+ *
+ *   q     [T, H, 192] BF16 (q_nope 128 | q_pe 64)
+ *   kv    [B, S_max, 576] BF16 (the latent cache of dsa_sparse_mla)
+ *   wkv_b [H, 256, 512] BF16 (per head: the 128 k_nope rows, then the 128 v rows)
+ *   out   [T, H, 128] BF16;  lse [T, H] fp32 or NULL
+ * 1 <= H <= 128; dtype must be DSA_BF16 (else DSA_ERR_UNSUPPORTED).
+ * ws >= dsa_mha_prefill_workspace_size(B, S_max, H) bytes (holds the
+ * decompressed keys and values, 512 bytes per (sequence, position, head)). */
+DSA_API dsa_status dsa_mha_prefill(const dsa_geom* geom, int32_t H, float sm_scale,
+                           const void* q, const void* kv, const void* wkv_b, dsa_dtype dtype,
+                           void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_mha_prefill_workspace_size(int32_t B, int32_t S_max, int32_t H);
+
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);
 

@@ -68,6 +68,8 @@ def load(path=None):
                                     vp, sz, vp]),
         "dsa_forward_paged_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
         "dsa_indexer_cache_append_paged": (i32, [gp, pp, vp, i32, vp, vp, vp]),
+        "dsa_mha_prefill": (i32, [gp, i32, f32, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
+        "dsa_mha_prefill_workspace_size": (sz, [i32, i32, i32]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -83,8 +85,8 @@ ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "d
                  "dsa_sparse_mla_workspace_size", "dsa_forward", "dsa_forward_workspace_size",
                  "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_indexer_scores_paged",
                  "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
-                 "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_status_string",
-                 "dsa_version")
+                 "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_mha_prefill",
+                 "dsa_mha_prefill_workspace_size", "dsa_status_string", "dsa_version")
 
 
 def _ptr(t):
@@ -341,3 +343,34 @@ def indexer_cache_append(geom, k_new, k_cache, k_scale_cache, stream=None, pages
         _check(lib.dsa_indexer_cache_append_paged(ctypes.byref(geom), ctypes.byref(pages), *args),
                "dsa_indexer_cache_append_paged")
     return k_cache, k_scale_cache
+
+
+def mha_prefill_workspace_size(B, S_max, H):
+    return int(load().dsa_mha_prefill_workspace_size(B, S_max, H))
+
+
+def mha_prefill(geom, q, kv, wkv_b, sm_scale, out=None, lse=None, ws=None, want_lse=True, stream=None):
+    """dsa_mha_prefill: MHA-mode prefill for sequences within top-k.
+    q [T, H, 192], kv [B, S_max, 576], wkv_b [H, 256, 512] (bf16).
+    Returns (out [T, H, 128], lse [T, H] or None)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    _dev(q, "q", bf)
+    _dev(kv, "kv", bf)
+    _dev(wkv_b, "wkv_b", bf)
+    _need(q.dim() == 3 and q.shape[0] == T and q.shape[2] == 192, "q must be [T, H, 192]")
+    H = q.shape[1]
+    _need(tuple(kv.shape) == (geom.B, geom.S_max, 576), "kv must be [B, S_max, 576]")
+    _need(tuple(wkv_b.shape) == (H, 256, 512), "wkv_b must be [H, 256, 512]")
+    if out is None:
+        out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    need = mha_prefill_workspace_size(geom.B, geom.S_max, H)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.dsa_mha_prefill(ctypes.byref(geom), H, float(sm_scale), _ptr(q), _ptr(kv), _ptr(wkv_b), BF16, _ptr(out),
+                             _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_mha_prefill")
+    return out, lse

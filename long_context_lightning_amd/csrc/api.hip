@@ -474,6 +474,39 @@ dsa_status dsa_indexer_cache_append_paged(const dsa_geom* geom, const dsa_pages*
   return cache_append_impl(geom, pages, k_new, k_dtype, k_pool, k_scale_pool, stream);
 }
 
+size_t dsa_mha_prefill_workspace_size(int32_t B, int32_t S_max, int32_t H) {
+  if (B < 1 || S_max < 1 || H < 1) return 0;
+  return mha_workspace_bytes(B, S_max, H) + kAlign;
+}
+
+dsa_status dsa_mha_prefill(const dsa_geom* geom, int32_t H, float sm_scale, const void* q, const void* kv,
+                           const void* wkv_b, dsa_dtype dtype, void* out, float* lse, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  if (!geom_ok(geom) || !q || !kv || !wkv_b || !out) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(wkv_b, 16) || !aligned(out, 16)) return DSA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return DSA_ERR_INVALID_ARG;
+  if (H < 1 || H > 128) return DSA_ERR_INVALID_ARG;
+  if (dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+  const size_t half = mha_workspace_bytes(geom->B, geom->S_max, H) / 2;
+  if (ws_bytes < dsa_mha_prefill_workspace_size(geom->B, geom->S_max, H) || !ws || !aligned(ws, kAlign))
+    return DSA_ERR_WORKSPACE;
+  MhaArgs a;
+  a.B = geom->B;
+  a.q_len = geom->q_len;
+  a.S_max = geom->S_max;
+  a.H = H;
+  a.seq_lens = geom->seq_lens;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.kv = kv;
+  a.wkv_b = wkv_b;
+  a.out = out;
+  a.lse = lse;
+  a.knope_ws = ws;
+  a.v_ws = static_cast<char*>(ws) + align_up(half);
+  return hip_status(launch_mha_prefill(a, stream));
+}
+
 const char* dsa_status_string(dsa_status s) {
   switch (s) {
     case DSA_OK: return "DSA_OK";

@@ -265,4 +265,21 @@ size_t mla_workspace_bytes(int T, int H, int k, int is_bf16);
 hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t s);
 hipError_t launch_mla_f32(const MlaArgs& a, hipStream_t s);
 
+// MHA-mode prefill (sequences within top-k): decompression of the latent
+// rows through wkv_b into the workspace, then causal attention.
+struct MhaArgs {
+  int B, q_len, S_max, H;
+  const int32_t* seq_lens;
+  float sm_scale;
+  const void* q;          // [T,H,192] bf16: q_nope | q_pe
+  const void* kv;         // [B,S_max,576] bf16: latent | k_pe
+  const void* wkv_b;      // [H,256,512] bf16: k_nope rows | v rows
+  void* out;              // [T,H,128] bf16
+  float* lse;             // [T,H] or null
+  void* knope_ws;         // [B,H,S_max,128] bf16
+  void* v_ws;             // [B,H,S_max,128] bf16
+};
+size_t mha_workspace_bytes(int B, int S_max, int H);
+hipError_t launch_mha_prefill(const MhaArgs& a, hipStream_t s);
+
 }  // namespace dsa

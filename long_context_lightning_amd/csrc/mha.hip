@@ -1,0 +1,388 @@
+// MHA-mode MLA prefill for sequences no longer than top-k.
+//
+// "详解DSA", section "DSA计算流 & 性能分析": prefill inside top-k runs in MHA
+// mode; the MLA forward code block there gives the MHA branch: wkv_b turns
+// each latent row into per-head [k_nope | v], the key of head h is
+// [k_nope_h, k_pe] with k_pe shared by the heads, softmax in fp32 over the
+// scores plus the masks, output scores @ v.  With L <= k the top-k keeps
+// every position (the charlestar page's short-prompt paragraph: nothing can
+// be cut, a masked MHA stands in for DSA), so what remains is causal
+// attention over the decompressed keys and values.  Per selected entry MHA
+// mode costs 128 x (192 + 128) x 2 flops against 128 x (576 + 512) x 2 in
+// MQA mode, which is why the pages take it for short prefills.
+//
+// Two kernels:
+//
+// k_mha_decompress: [k_nope | v] = latent . wkv_b^T per head, a bf16 GEMM on
+//   v_mfma_f32_16x16x32_bf16.  A block computes 128 positions x one 128-wide
+//   half (k_nope or v) of one head; 4 waves of 64 x 64.  64-deep K chunks of
+//   both operands go global -> LDS by DMA (double buffered), 16-byte pieces
+//   XOR-swizzled so the 16 rows one fragment read covers fall on distinct
+//   banks.  Output head-major: k_nope[b][h][s][128], v[b][h][s][128] bf16.
+//
+// k_mha_attn: one block = one head x 256 consecutive queries of one
+//   sequence, 8 waves (two per SIMD) of 32 queries.  Keys stream in 64-key
+//   tiles through a 3-slot LDS ring (DMA; a K row is [k_nope_h | k_pe] =
+//   384 bytes, a V row 256 bytes, both swizzled).  Per tile and wave:
+//     S^T[64 keys x 32 queries] = K . Q^T   (Q^T fragments in registers),
+//   so a lane holds one query column: the online softmax (fp32, base 2) and
+//   its rescaling are per lane, and the bf16 weights stay in registers as the
+//   B operand of
+//     O^T[128 dims x 32 queries] += V^T . P^T
+//   with V^T read by the LDS transpose load (keys in the order the score
+//   fragments hold them).  Causal: keys past a query's position are -inf;
+//   tiles past a wave's last query are skipped by that wave.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kDN = 128, kDR = 64, kDQh = kDN + kDR, kDVh = 128, kDL = 512;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v8bf as_v8bf(v4i x) { return __builtin_bit_cast(v8bf, x); }
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// four fp32 -> four bf16 (RNE), packed
+__device__ __forceinline__ uint2 pack4_bf16(float x0, float x1, float x2, float x3) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x0, x1}, v2bf));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){x2, x3}, v2bf));
+  return uint2{lo, hi};
+}
+
+// ------------------------------------------------------------ decompression
+
+constexpr int kGT = 128;                 // positions (and output columns) per block
+constexpr int kGK = 64;                  // K depth per stage
+constexpr int kGRow = 2 * kGK;           // bytes of one row of a stage (128)
+constexpr int kGOp = kGT * kGRow;        // one operand's stage (16 KB)
+constexpr int kGStage = 2 * kGOp;        // W and latent
+constexpr int kGSteps = kDL / kGK;       // 8
+constexpr int kGDma = 2 * kGOp / 1024 / 4;  // DMA instructions per wave per stage (8)
+
+// Stage kc of the block's operands: W rows (output columns) then latent rows
+// (positions), 128 bytes per row; lane l of instruction i fills 16-byte slot
+// 64i + l, i.e. row r = slot / 8, stored piece p = slot % 8, which holds the
+// row's logical piece p ^ ((r >> 1) & 7).
+__device__ __forceinline__ void gemm_stage(const MhaArgs& a, int b, int h, int half, int s0, int L, int kc,
+                                           uint32_t stage_off, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < kGDma; ++u) {
+    const int i = wave * kGDma + u;          // 0..31: 0..15 W, 16..31 latent
+    const int slot = 64 * (i & 15) + lane;
+    const int r = slot >> 3, p = slot & 7;
+    const int piece = p ^ ((r >> 1) & 7);
+    const char* src;
+    if (i < 16) {
+      src = reinterpret_cast<const char*>(a.wkv_b) +
+            (((size_t)h * 2 * kDVh + (size_t)half * kDVh + r) * kDL + (size_t)kc * kGK + 8 * piece) * 2;
+    } else {
+      const int s = min(s0 + r, L - 1);
+      src = reinterpret_cast<const char*>(a.kv) +
+            (((size_t)b * a.S_max + s) * kDQK + (size_t)kc * kGK + 8 * piece) * 2;
+    }
+    dma16_lds_at(src, stage_off + (i < 16 ? 0 : kGOp) + 1024 * (i & 15));
+  }
+}
+
+__global__ __launch_bounds__(256, 2) void k_mha_decompress(MhaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kGStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.z, h = blockIdx.y >> 1, half = blockIdx.y & 1;
+  const int L = clamped_len(a.seq_lens, b, a.S_max);
+  const int s0 = blockIdx.x * kGT;
+  if (s0 >= L) return;
+  const uint32_t base = lds_offset(lds);
+  const int wn = wave & 1, wsb = wave >> 1;  // 64-column block, 64-position block
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  gemm_stage(a, b, h, half, s0, L, 0, base, wave, lane);
+  for (int kc = 0; kc < kGSteps; ++kc) {
+    if (kc + 1 < kGSteps) {
+      gemm_stage(a, b, h, half, s0, L, kc + 1, base + ((kc + 1) & 1) * kGStage, wave, lane);
+      vm_wait<kGDma>();
+    } else {
+      vm_wait<0>();
+    }
+    lds_barrier();
+    const unsigned char* st = lds + (kc & 1) * kGStage;
+#pragma unroll
+    for (int kk = 0; kk < kGK / 32; ++kk) {
+      v8bf wf[4], xf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rw = 64 * wn + 16 * j + c;   // output column (W row)
+        const int rx = 64 * wsb + 16 * j + c;  // position (latent row)
+        const int pc = 4 * kk + g;             // logical piece
+        wf[j] = as_v8bf(*reinterpret_cast<const v4i*>(st + rw * kGRow + 16 * (pc ^ ((rw >> 1) & 7))));
+        xf[j] = as_v8bf(*reinterpret_cast<const v4i*>(st + kGOp + rx * kGRow + 16 * (pc ^ ((rx >> 1) & 7))));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+    }
+    lds_barrier();  // the next step refills this stage
+  }
+  // D[column 4g + i][position c] of block (i, j): four consecutive columns of
+  // one position per lane -> one 8-byte store.
+  uint16_t* dst = static_cast<uint16_t*>(half ? a.v_ws : a.knope_ws) + ((size_t)b * a.H + h) * a.S_max * kDVh;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int s = s0 + 64 * wsb + 16 * j + c;
+    if (s >= L) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint2 pk = pack4_bf16(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      *reinterpret_cast<uint2*>(dst + (size_t)s * kDVh + 64 * wn + 16 * i + 4 * g) = pk;
+    }
+  }
+}
+
+// ------------------------------------------------------------ attention
+
+constexpr int kAW = 8;                    // waves per block (two per SIMD)
+constexpr int kAQW = 32;                  // queries per wave
+constexpr int kAQ = kAW * kAQW;           // queries per block
+constexpr int kAK = 64;                   // keys per tile
+constexpr int kKRow = 2 * kDQh;           // 384 bytes: [k_nope_h | k_pe]
+constexpr int kKTile = kAK * kKRow;       // 24 KB
+constexpr int kVRow = 2 * kDVh;           // 256 bytes
+constexpr int kVTile = kAK * kVRow;       // 16 KB
+constexpr int kAStage = kKTile + kVTile;  // 40 KB
+constexpr int kASlots = 3;
+constexpr int kKInstr = kKTile / 1024;    // 24
+constexpr int kVInstr = kVTile / 1024;    // 16
+constexpr int kADma = (kKInstr + kVInstr) / kAW;  // 5 per wave per tile
+static_assert(kADma * kAW == kKInstr + kVInstr, "whole DMA share per wave");
+
+// Tile of keys s0 .. s0+63 into a ring slot.  K slot 64i + l holds row
+// r = slot / 24, stored piece p = slot % 24 = logical piece p ^ ((r >> 1) & 7)
+// (pieces 0..15: k_nope of head h from the workspace, 16..23: k_pe from the
+// latent cache).  V slot 64i + l holds row r = slot / 16, stored piece
+// slot % 16 = logical piece p ^ (2 * (r & 3)).  Keys past the sequence read
+// its last row (masked later).
+__device__ __forceinline__ void attn_tile(const MhaArgs& a, const uint16_t* knope, const uint16_t* vv, int b,
+                                          int s0, int L, uint32_t slot_off, int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < kADma; ++u) {
+    const int i = wave * kADma + u;
+    const char* src;
+    uint32_t dst;
+    if (i < kKInstr) {
+      const int slot = 64 * i + lane;
+      const int r = slot / 24, p = slot - 24 * r;
+      const int piece = p ^ ((r >> 1) & 7);
+      const int s = min(s0 + r, L - 1);
+      src = piece < 16 ? reinterpret_cast<const char*>(knope + (size_t)s * kDN + 8 * piece)
+                       : reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.kv) +
+                                                       ((size_t)b * a.S_max + s) * kDQK + kDL + 8 * (piece - 16));
+      dst = slot_off + 1024 * i;
+    } else {
+      const int iv = i - kKInstr;
+      const int slot = 64 * iv + lane;
+      const int r = slot >> 4, p = slot & 15;
+      const int piece = p ^ (2 * (r & 3));
+      const int s = min(s0 + r, L - 1);
+      src = reinterpret_cast<const char*>(vv + (size_t)s * kDVh + 8 * piece);
+      dst = slot_off + kKTile + 1024 * iv;
+    }
+    dma16_lds_at(src, dst);
+  }
+}
+
+__global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kASlots * kAStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest query tiles first
+  const int L = clamped_len(a.seq_lens, b, a.S_max);
+  const int i0 = qt * kAQ;                               // first query index within the sequence
+  const int i1 = min(i0 + kAQ, a.q_len);
+  if (i0 >= i1) return;
+  const int pos0 = L - a.q_len;                          // position of query index 0
+  const int maxpos = pos0 + i1 - 1;
+  const int ntiles = maxpos < 0 ? 0 : maxpos / kAK + 1;
+  const int wi0 = i0 + kAQW * wave;                      // this wave's first query index
+  const int w_minpos = pos0 + wi0;
+  const int w_maxpos = wi0 < i1 ? pos0 + min(wi0 + kAQW, i1) - 1 : -1;  // -1: the wave has no query
+  const uint16_t* knope = static_cast<const uint16_t*>(a.knope_ws) + ((size_t)b * a.H + h) * a.S_max * kDN;
+  const uint16_t* vv = static_cast<const uint16_t*>(a.v_ws) + ((size_t)b * a.H + h) * a.S_max * kDVh;
+  const uint32_t ring_off = lds_offset(ring);
+
+  if (ntiles > 0) attn_tile(a, knope, vv, b, 0, L, ring_off, wave, lane);
+  if (ntiles > 1) attn_tile(a, knope, vv, b, kAK, L, ring_off + kAStage, wave, lane);
+
+  // Q^T fragments: lane (g, c) supplies query wi0 + 16 qb + c, dims 32 ks + 8g .. +7.
+  v8bf qf[2][kDQh / 32];
+  int qpos[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = wi0 + 16 * qb + c;
+    const bool on = qi < i1;
+    qpos[qb] = on ? pos0 + qi : -1;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + ((size_t)(b * a.q_len + (on ? qi : i0)) * a.H + h) * kDQh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDQh / 32; ++ks)
+      qf[qb][ks] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
+  }
+
+  const float qk_scale = a.sm_scale * kLog2e;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  v4f acc[kDVh / 16][2];
+#pragma unroll
+  for (int db = 0; db < kDVh / 16; ++db) acc[db][0] = acc[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // V^T read of lane (g, c): key row 4g + c/4 (+16), bytes 8 (c & 3) of value
+  // block db, i.e. logical piece 2 db + (c & 3) / 2, half c & 1.
+  const int vrow = 4 * g + (c >> 2);
+  for (int n = 0; n < ntiles; ++n) {
+    if (n + 1 < ntiles) vm_wait<kADma>();
+    else vm_wait<0>();
+    lds_barrier();  // tile n landed everywhere; every wave is done with tile n - 1
+    if (n + 2 < ntiles) attn_tile(a, knope, vv, b, (n + 2) * kAK, L, ring_off + ((n + 2) % kASlots) * kAStage, wave, lane);
+    const int s0 = n * kAK;
+    if (s0 > w_maxpos) continue;  // every key of the tile is past this wave's queries
+    const unsigned char* kt = ring + (n % kASlots) * kAStage;
+    const unsigned char* vt = kt + kKTile;
+
+    // scores
+    v4f sa[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sa[kb][0] = sa[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDQh / 32; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int r = 16 * kb + c;
+        const v8bf kf = as_v8bf(*reinterpret_cast<const v4i*>(kt + r * kKRow + 16 * ((4 * ks + g) ^ ((r >> 1) & 7))));
+        sa[kb][0] = mfma_bf16(kf, qf[0][ks], sa[kb][0]);
+        sa[kb][1] = mfma_bf16(kf, qf[1][ks], sa[kb][1]);
+      }
+    }
+
+    // online softmax per query column (this lane: query c of block qb; keys
+    // 16 kb + 4g + i)
+    const bool diag = s0 + kAK - 1 > w_minpos;
+    v8bf pf[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float sv[16];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = s0 + 16 * kb + 4 * g + i;
+          sv[4 * kb + i] = (!diag || key <= qpos[qb]) ? sa[kb][qb][i] * qk_scale : -INFINITY;
+        }
+      float tmax = sv[0];
+#pragma unroll
+      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sv[j]);
+      tmax = max_xor32(max_xor16(tmax));
+      const float m_new = fmaxf(m_run[qb], tmax);
+      if (m_new == -INFINITY) {  // nothing visible yet for this query
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) pf[kk][qb] = as_v8bf(v4i{0, 0, 0, 0});
+        continue;
+      }
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 0 when m_run = -inf
+      m_run[qb] = m_new;
+      uint32_t pk[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(sv[2 * j] - m_new);
+        const float p1 = __builtin_amdgcn_exp2f(sv[2 * j + 1] - m_new);
+        pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2bf));
+        psum += __uint_as_float(pk[j] << 16) + __uint_as_float(pk[j] & 0xFFFF0000u);
+      }
+      l_run[qb] = l_run[qb] * alpha + psum;
+      if (alpha != 1.f) {
+#pragma unroll
+        for (int db = 0; db < kDVh / 16; ++db) acc[db][qb] *= alpha;
+      }
+      // k-slots 8g .. 8g+7 of value step kk = keys {4g..4g+3} of block 2kk
+      // and {4g..4g+3} of block 2kk + 1
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        pf[kk][qb] = __builtin_bit_cast(
+            v8bf, v4i{(int)pk[4 * kk], (int)pk[4 * kk + 1], (int)pk[4 * kk + 2], (int)pk[4 * kk + 3]});
+    }
+
+    // values: V^T fragment (16 dims x the 32 keys of step kk) feeds both
+    // query blocks
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int db = 0; db < kDVh / 16; ++db) {
+        const int piece = 2 * db + ((c & 3) >> 1);
+        const int r0 = 32 * kk + vrow, r1 = r0 + 16;
+        const unsigned char* p0 = vt + r0 * kVRow + 16 * (piece ^ (2 * (r0 & 3))) + 8 * (c & 1);
+        const unsigned char* p1 = vt + r1 * kVRow + 16 * (piece ^ (2 * (r1 & 3))) + 8 * (c & 1);
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+        const v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[db][0] = mfma_bf16(vf, pf[kk][0], acc[db][0]);
+        acc[db][1] = mfma_bf16(vf, pf[kk][1], acc[db][1]);
+      }
+    }
+  }
+
+  // out[t, h, dims 16 db + 4g .. +3] for query c of block qb; lse by the g = 0 lanes
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = wi0 + 16 * qb + c;
+    if (qi >= i1) continue;
+    const float l = sum_xor32(sum_xor16(l_run[qb]));
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t t = (size_t)b * a.q_len + qi;
+    uint16_t* orow = static_cast<uint16_t*>(a.out) + (t * a.H + h) * kDVh;
+#pragma unroll
+    for (int db = 0; db < kDVh / 16; ++db) {
+      const v4f o = acc[db][qb];
+      *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = pack4_bf16(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    }
+    if (a.lse && g == 0) a.lse[t * a.H + h] = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace
+
+size_t mha_workspace_bytes(int B, int S_max, int H) { return (size_t)2 * B * H * S_max * kDVh * sizeof(uint16_t); }
+
+hipError_t launch_mha_prefill(const MhaArgs& a, hipStream_t stream) {
+  const dim3 g1((unsigned)((a.S_max + kGT - 1) / kGT), (unsigned)(2 * a.H), (unsigned)a.B);
+  hipLaunchKernelGGL(k_mha_decompress, g1, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2((unsigned)((a.q_len + kAQ - 1) / kAQ), (unsigned)a.H, (unsigned)a.B);
+  hipLaunchKernelGGL(k_mha_attn, g2, dim3(kAW * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

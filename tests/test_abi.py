@@ -167,3 +167,21 @@ def test_paged_validation():
     app = lambda pg: lib.dsa_indexer_cache_append_paged(ctypes.byref(g), pg, P(FAKE), 1, P(FAKE), P(FAKE), None)
     assert app(None) == 1
     assert app(ctypes.byref(_pages(max_pages=4, page_size=100))) == 1
+
+
+def test_mha_prefill_validation():
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=4, S=64)
+    need = lib.dsa_mha_prefill_workspace_size(2, 64, 16)
+    assert need >= 2 * 2 * 16 * 64 * 128 * 2                                  # decompressed k_nope and v
+    call = lambda H, dt, ws, wsb: lib.dsa_mha_prefill(ctypes.byref(g), H, 0.1, P(FAKE), P(FAKE), P(FAKE), dt,
+                                                      P(FAKE), None, P(ws), wsb, None)
+    assert call(16, 0, FAKE, need) == 2        # f32 not offered
+    assert call(0, 1, FAKE, need) == 1
+    assert call(129, 1, FAKE, need) == 1
+    assert call(16, 1, FAKE, need - 1) == 3
+    assert call(16, 1, FAKE + 16, need) == 3   # workspace alignment
+    assert lib.dsa_mha_prefill(ctypes.byref(g), 16, 0.1, P(FAKE + 8), P(FAKE), P(FAKE), 1, P(FAKE), None, P(FAKE),
+                               need, None) == 1
+    assert lib.dsa_mha_prefill_workspace_size(0, 64, 16) == 0

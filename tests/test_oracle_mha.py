@@ -9,14 +9,16 @@ than its own formula:
   fresh prefill, with keys and values built from the decompression;
 * closed forms: a query at position 0 returns its value row and lse = its one
   score; equal keys give equal weights;
-* one element of the decompression summed by hand.
+* one element of the decompression summed by hand;
+* the bf16 rounding of the decompressed rows against torch's float64 ->
+  bfloat16 cast (round to nearest even), ties included.
 """
 
 import numpy as np
 import torch
 
 from oracle import mha_prefill, mha_decompress, sparse_mla
-from oracle.mha import D_LATENT, D_NOPE, D_ROPE, D_V
+from oracle.mha import D_LATENT, D_NOPE, D_ROPE, D_V, round_to_bf16
 
 
 def _inputs(rng, B, q_len, S, H):
@@ -95,3 +97,18 @@ def test_decompression_element_by_hand():
         assert abs(k_nope[b, s, h, j] - want) < 1e-9
         want_v = sum(float(w[h, D_NOPE + j, c]) * float(kv[b, s, c]) for c in range(D_LATENT))
         assert abs(v[b, s, h, j] - want_v) < 1e-9
+
+
+def test_bf16_rounding_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(20000) * 2.0 ** rng.integers(-20, 20, 20000)
+    # exact midpoints between neighbouring bf16 values (ties) in both directions
+    base = rng.integers(0x3F00, 0x4100, 2000).astype(np.uint32) << 16
+    mids = (base | 0x8000).view(np.float32).astype(np.float64)
+    x = np.concatenate([x, mids, -mids, [0.0, -0.0, 1.0, 3.0e38]])
+    want = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_to_bf16(x), want)
+    q, kv, w = _inputs(rng, 1, 1, 6, 2)
+    k_exact, v_exact = mha_decompress(kv, "f32", w, "f32")
+    k_r, v_r = mha_decompress(kv, "f32", w, "f32", round_bf16=True)
+    assert np.array_equal(k_r, round_to_bf16(k_exact)) and np.array_equal(v_r, round_to_bf16(v_exact))
