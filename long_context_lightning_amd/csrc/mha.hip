@@ -23,15 +23,20 @@
 // k_mha_attn: one block = one head x 256 consecutive queries of one
 //   sequence, 8 waves (two per SIMD) of 32 queries.  Keys stream in 64-key
 //   tiles through a 3-slot LDS ring (DMA; a K row is [k_nope_h | k_pe] =
-//   384 bytes, a V row 256 bytes, both swizzled).  Per tile and wave:
+//   384 bytes with XOR-swizzled pieces, a V row 256 bytes padded to 288 so
+//   the 8 rows one transpose read covers fall on distinct banks).  Per tile
+//   and wave:
 //     S^T[64 keys x 32 queries] = K . Q^T   (Q^T fragments in registers),
 //   so a lane holds one query column: the online softmax (fp32, base 2) and
 //   its rescaling are per lane, and the bf16 weights stay in registers as the
 //   B operand of
 //     O^T[128 dims x 32 queries] += V^T . P^T
 //   with V^T read by the LDS transpose load (keys in the order the score
-//   fragments hold them).  Causal: keys past a query's position are -inf;
-//   tiles past a wave's last query are skipped by that wave.
+//   fragments hold them).  The softmax reference moves only when a tile's
+//   maximum passes it by more than 2^8, so the accumulators are rarely
+//   rescaled; the normaliser sums the bf16-rounded weights the value product
+//   uses.  Causal: keys past a query's position are -inf (diagonal tiles
+//   only); tiles past a wave's last query are skipped by that wave.
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -169,26 +174,29 @@ constexpr int kAQ = kAW * kAQW;           // queries per block
 constexpr int kAK = 64;                   // keys per tile
 constexpr int kKRow = 2 * kDQh;           // 384 bytes: [k_nope_h | k_pe]
 constexpr int kKTile = kAK * kKRow;       // 24 KB
-constexpr int kVRow = 2 * kDVh;           // 256 bytes
-constexpr int kVTile = kAK * kVRow;       // 16 KB
-constexpr int kAStage = kKTile + kVTile;  // 40 KB
+constexpr int kVPieces = 18;              // 16 pieces of 16 bytes + 32 bytes of padding
+constexpr int kVRow = 16 * kVPieces;      // 288 bytes: consecutive rows 32 bytes apart mod 256
+constexpr int kVTile = kAK * kVRow;       // 18 KB
+constexpr int kAStage = kKTile + kVTile;  // 42 KB
 constexpr int kASlots = 3;
 constexpr int kKInstr = kKTile / 1024;    // 24
-constexpr int kVInstr = kVTile / 1024;    // 16
-constexpr int kADma = (kKInstr + kVInstr) / kAW;  // 5 per wave per tile
-static_assert(kADma * kAW == kKInstr + kVInstr, "whole DMA share per wave");
+constexpr int kVInstr = kVTile / 1024;    // 18
+constexpr int kAInstr = kKInstr + kVInstr;  // 42: waves 0, 1 issue 6 per tile, the others 5
+constexpr float kRescaleMargin = 8.f;     // log2 units the running reference may lag the maximum
 
-// Tile of keys s0 .. s0+63 into a ring slot.  K slot 64i + l holds row
-// r = slot / 24, stored piece p = slot % 24 = logical piece p ^ ((r >> 1) & 7)
-// (pieces 0..15: k_nope of head h from the workspace, 16..23: k_pe from the
-// latent cache).  V slot 64i + l holds row r = slot / 16, stored piece
-// slot % 16 = logical piece p ^ (2 * (r & 3)).  Keys past the sequence read
-// its last row (masked later).
+// Tile of keys s0 .. s0+63 into a ring slot; wave w issues instructions
+// w, w + 8, ...  K slot 64i + l holds row r = slot / 24, stored piece
+// p = slot % 24 = logical piece p ^ ((r >> 1) & 7) (pieces 0..15: k_nope of
+// head h from the workspace, 16..23: k_pe from the latent cache).  V slot
+// 64i' + l holds row r = slot / 18, piece slot % 18 (16, 17: padding, filled
+// with a copy of piece 0).  Keys past the sequence read its last row
+// (masked later).
 __device__ __forceinline__ void attn_tile(const MhaArgs& a, const uint16_t* knope, const uint16_t* vv, int b,
                                           int s0, int L, uint32_t slot_off, int wave, int lane) {
 #pragma unroll
-  for (int u = 0; u < kADma; ++u) {
-    const int i = wave * kADma + u;
+  for (int u = 0; u < 6; ++u) {
+    const int i = wave + kAW * u;
+    if (i >= kAInstr) break;  // wave-uniform
     const char* src;
     uint32_t dst;
     if (i < kKInstr) {
@@ -203,10 +211,9 @@ __device__ __forceinline__ void attn_tile(const MhaArgs& a, const uint16_t* knop
     } else {
       const int iv = i - kKInstr;
       const int slot = 64 * iv + lane;
-      const int r = slot >> 4, p = slot & 15;
-      const int piece = p ^ (2 * (r & 3));
+      const int r = slot / kVPieces, p = slot - kVPieces * r;
       const int s = min(s0 + r, L - 1);
-      src = reinterpret_cast<const char*>(vv + (size_t)s * kDVh + 8 * piece);
+      src = reinterpret_cast<const char*>(vv + (size_t)s * kDVh + (p < 16 ? 8 * p : 0));
       dst = slot_off + kKTile + 1024 * iv;
     }
     dma16_lds_at(src, dst);
@@ -252,26 +259,46 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
       qf[qb][ks] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
   }
 
+  // Per-lane LDS offsets inside a slot, kept opaque so every read below is
+  // one base register plus an immediate.  K read of row 16 kb + c, logical
+  // piece 4 ks + g, stored at piece (4 ks + g) ^ y with y = (c >> 1) & 7:
+  // = 4 (ks ^ (y >> 2)) + (g ^ (y & 3)), so even and odd ks each need one
+  // base.  V^T read of row 32 kk + 4g + c/4 (+16), bytes 32 db + 8 (c & 3).
+  const int y = (c >> 1) & 7;
+  int kbase0 = c * kKRow + 16 * (4 * (0 ^ (y >> 2)) + (g ^ (y & 3)));
+  int kbase1 = c * kKRow + 16 * (4 * (1 ^ (y >> 2)) + (g ^ (y & 3)));
+  int vbase = kKTile + (4 * g + (c >> 2)) * kVRow + 8 * (c & 3);
+  asm volatile("" : "+v"(kbase0), "+v"(kbase1), "+v"(vbase));
+
+  // The Q loads (and the first two tiles) complete before the loop, so the
+  // compiler keeps no memory wait inside it: the only waits there are the
+  // explicit ones that leave the next tile's copies in flight.
+  vm_wait<0>();
+
   const float qk_scale = a.sm_scale * kLog2e;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  // m_ref: the reference the weights are taken against (log2 units); it
+  // moves only when a tile's maximum passes it by more than kRescaleMargin,
+  // so weights stay below 2^8 and the accumulators are rescaled rarely.
+  float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
   v4f acc[kDVh / 16][2];
 #pragma unroll
   for (int db = 0; db < kDVh / 16; ++db) acc[db][0] = acc[db][1] = v4f{0.f, 0.f, 0.f, 0.f};
+  const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // V^T read of lane (g, c): key row 4g + c/4 (+16), bytes 8 (c & 3) of value
-  // block db, i.e. logical piece 2 db + (c & 3) / 2, half c & 1.
-  const int vrow = 4 * g + (c >> 2);
   for (int n = 0; n < ntiles; ++n) {
-    if (n + 1 < ntiles) vm_wait<kADma>();
-    else vm_wait<0>();
+    if (n + 1 < ntiles) {
+      if (wave < kAInstr - 5 * kAW) vm_wait<6>();
+      else vm_wait<5>();
+    } else {
+      vm_wait<0>();
+    }
     lds_barrier();  // tile n landed everywhere; every wave is done with tile n - 1
     if (n + 2 < ntiles) attn_tile(a, knope, vv, b, (n + 2) * kAK, L, ring_off + ((n + 2) % kASlots) * kAStage, wave, lane);
     const int s0 = n * kAK;
     if (s0 > w_maxpos) continue;  // every key of the tile is past this wave's queries
     const unsigned char* kt = ring + (n % kASlots) * kAStage;
-    const unsigned char* vt = kt + kKTile;
 
-    // scores
+    // scores S^T[key 16 kb + 4g + i][query 16 qb + c]
     v4f sa[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sa[kb][0] = sa[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -279,73 +306,67 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
     for (int ks = 0; ks < kDQh / 32; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int r = 16 * kb + c;
-        const v8bf kf = as_v8bf(*reinterpret_cast<const v4i*>(kt + r * kKRow + 16 * ((4 * ks + g) ^ ((r >> 1) & 7))));
+        const unsigned char* p = kt + ((ks & 1) ? kbase1 : kbase0) + 16 * kKRow * kb + 128 * (ks >> 1);
+        const v8bf kf = as_v8bf(*reinterpret_cast<const v4i*>(p));
         sa[kb][0] = mfma_bf16(kf, qf[0][ks], sa[kb][0]);
         sa[kb][1] = mfma_bf16(kf, qf[1][ks], sa[kb][1]);
       }
     }
+    if (s0 + kAK - 1 > w_minpos) {  // diagonal tile: keys past a query's position are -inf
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (s0 + 16 * kb + 4 * g + i > qpos[qb]) sa[kb][qb][i] = -INFINITY;
+    }
 
-    // online softmax per query column (this lane: query c of block qb; keys
-    // 16 kb + 4g + i)
-    const bool diag = s0 + kAK - 1 > w_minpos;
+    // weights 2^(s * scale - m_ref), rounded to bf16; k-slots 8g .. 8g+7 of
+    // value step kk hold keys {4g..4g+3} of block 2kk and of block 2kk + 1
     v8bf pf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float sv[16];
+      float tmax = fmaxf(fmaxf(sa[0][qb][0], sa[0][qb][1]), fmaxf(sa[0][qb][2], sa[0][qb][3]));
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = s0 + 16 * kb + 4 * g + i;
-          sv[4 * kb + i] = (!diag || key <= qpos[qb]) ? sa[kb][qb][i] * qk_scale : -INFINITY;
-        }
-      float tmax = sv[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) tmax = fmaxf(tmax, sv[j]);
-      tmax = max_xor32(max_xor16(tmax));
-      const float m_new = fmaxf(m_run[qb], tmax);
-      if (m_new == -INFINITY) {  // nothing visible yet for this query
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) pf[kk][qb] = as_v8bf(v4i{0, 0, 0, 0});
-        continue;
-      }
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);  // 0 when m_run = -inf
-      m_run[qb] = m_new;
-      uint32_t pk[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(sv[2 * j] - m_new);
-        const float p1 = __builtin_amdgcn_exp2f(sv[2 * j + 1] - m_new);
-        pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2bf));
-        psum += __uint_as_float(pk[j] << 16) + __uint_as_float(pk[j] & 0xFFFF0000u);
-      }
-      l_run[qb] = l_run[qb] * alpha + psum;
-      if (alpha != 1.f) {
+      for (int kb = 1; kb < 4; ++kb)
+        tmax = fmaxf(tmax, fmaxf(fmaxf(sa[kb][qb][0], sa[kb][qb][1]), fmaxf(sa[kb][qb][2], sa[kb][qb][3])));
+      tmax = max_xor32(max_xor16(tmax)) * qk_scale;  // the scale is positive
+      if (tmax > m_ref[qb] + kRescaleMargin) {       // rare: move the reference
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[qb] - tmax);  // 0 while nothing is accumulated
+        m_ref[qb] = tmax;
+        l_run[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < kDVh / 16; ++db) acc[db][qb] *= alpha;
       }
-      // k-slots 8g .. 8g+7 of value step kk = keys {4g..4g+3} of block 2kk
-      // and {4g..4g+3} of block 2kk + 1
+      const float nm = m_ref[qb] == -INFINITY ? 0.f : -m_ref[qb];  // all -inf so far: weights 0
+      uint32_t pk[8];
+      float psum = l_run[qb];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[j >> 1][qb][2 * (j & 1)], qk_scale, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[j >> 1][qb][2 * (j & 1) + 1], qk_scale, nm));
+        const v2bf pb = __builtin_convertvector((v2f){p0, p1}, v2bf);
+        pk[j] = __builtin_bit_cast(uint32_t, pb);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, psum, false);  // the rounded weights
+      }
+      l_run[qb] = psum;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
         pf[kk][qb] = __builtin_bit_cast(
             v8bf, v4i{(int)pk[4 * kk], (int)pk[4 * kk + 1], (int)pk[4 * kk + 2], (int)pk[4 * kk + 3]});
     }
 
-    // values: V^T fragment (16 dims x the 32 keys of step kk) feeds both
+    // values: the V^T fragment (16 dims x the 32 keys of step kk) feeds both
     // query blocks
+    const unsigned char* vt = kt + vbase;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int db = 0; db < kDVh / 16; ++db) {
-        const int piece = 2 * db + ((c & 3) >> 1);
-        const int r0 = 32 * kk + vrow, r1 = r0 + 16;
-        const unsigned char* p0 = vt + r0 * kVRow + 16 * (piece ^ (2 * (r0 & 3))) + 8 * (c & 1);
-        const unsigned char* p1 = vt + r1 * kVRow + 16 * (piece ^ (2 * (r1 & 3))) + 8 * (c & 1);
+        const unsigned char* p0 = vt + 32 * kk * kVRow + 32 * db;
         const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 16 * kVRow));
         const v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db][0] = mfma_bf16(vf, pf[kk][0], acc[db][0]);
         acc[db][1] = mfma_bf16(vf, pf[kk][1], acc[db][1]);
@@ -367,7 +388,7 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
       const v4f o = acc[db][qb];
       *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = pack4_bf16(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     }
-    if (a.lse && g == 0) a.lse[t * a.H + h] = l > 0.f ? (m_run[qb] + log2f(l)) * kLn2 : -INFINITY;
+    if (a.lse && g == 0) a.lse[t * a.H + h] = l > 0.f ? (m_ref[qb] + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
