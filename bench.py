@@ -197,6 +197,9 @@ def main():
     # ------------------------------------------- fp8 quantisation / append
     quant = bench_quant(lcl, torch, dev, stream, evict, wl)
 
+    # ------------------------------------ short prefill: MHA mode vs MQA mode
+    mha = bench_mha(lcl, torch, dev, stream, evict)
+
     # --------------------------------------------------------- prefill 64K
     prefill = None
     if not args.no_prefill:
@@ -230,6 +233,7 @@ def main():
         "stages": stages,
         "quantize": quant,
         "paged": paged,
+        "mha_prefill": mha,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
@@ -297,6 +301,66 @@ def bench_paged(args, lcl, torch, np, dev, stream, evict, wl, d, geom, idx, out,
     return {"page_size": P, "num_pages": int(num_pages), "us_per_step": round(us["forward"], 2),
             "queries_per_s": round(qps, 1), "vs_contiguous_step": round(us["forward"] / (contiguous_ms * 1e3), 4),
             "indexer_us": round(us["indexer"], 2), "sparse_mla_us": round(us["sparse_mla"], 2)}
+
+
+def bench_mha(lcl, torch, dev, stream, evict, steps=5):
+    """Prefill of 4 prompts of 2048 tokens (= top-k, so every position is
+    kept) with 128 heads, both ways: dsa_mha_prefill (MHA mode: wkv_b
+    decompression + causal attention over 192/128-dim heads) and dsa_forward
+    in MQA mode on the absorbed shapes (the indexer is bypassed there, since
+    S_max <= top-k; the attention covers every position with 576/512-dim
+    entries).  Inputs drawn on the GPU with torch's seeded generator: q, the
+    latent cache and the MQA queries ~ N(0,1) bf16, wkv_b ~ N(0, 1/512) bf16.
+    Each call is timed after a last-level cache eviction (mean of `steps`)."""
+    B, L, H, k = 4, 2048, 128, 2048
+    T = B * L
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    q = torch.randn((T, H, 192), generator=g, device=dev).to(torch.bfloat16)
+    kv = torch.randn((B, L, 576), generator=g, device=dev).to(torch.bfloat16)
+    w = (torch.randn((H, 256, 512), generator=g, device=dev) / math.sqrt(512.0)).to(torch.bfloat16)
+    seq = torch.full((B,), L, dtype=torch.int32, device=dev)
+    geom = lcl.make_geom(B, L, L, seq)
+    out = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lcl.mha_prefill_workspace_size(B, L, H), dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(192.0)
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(steps):
+            evict()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]) * 1e3)
+        return sum(ts) / len(ts)
+
+    mha_us = timed(lambda: lcl.mha_prefill(geom, q, kv, w, sm, out=out, ws=ws, want_lse=False))
+    del q, out, ws
+    qm = torch.randn((T, H, 576), generator=g, device=dev).to(torch.bfloat16)
+    qi = torch.zeros((T, 64, 128), dtype=torch.uint8, device=dev)     # unused: the indexer is bypassed
+    wi = torch.zeros((T, 64), dtype=torch.bfloat16, device=dev)
+    ki = torch.zeros((B, L, 128), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    outm = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    fws = torch.empty(lcl.forward_workspace_size(B, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16), dtype=torch.uint8,
+                      device=dev)
+    mqa_us = timed(lambda: lcl.forward(geom, k, sm, qi, wi, ki, qm, kv, idx=idx, out=outm, ws=fws, want_lse=False))
+    del qm, qi, wi, ki, idx, outm, fws
+    torch.cuda.empty_cache()
+    pairs = B * L * (L + 1) // 2
+    mha_flop = B * L * H * 256 * 512 * 2 + pairs * H * (192 + 128) * 2
+    mqa_flop = pairs * H * (576 + 512) * 2
+    log(f"short prefill 4 x 2048 (<= top-k): MHA mode {mha_us:.1f} us ({mha_flop / 1e12:.3f} TFLOP, "
+        f"{mha_flop / (mha_us * 1e-6) / 1e12:.1f} TFLOP/s); MQA-mode forward {mqa_us:.1f} us "
+        f"({mqa_flop / 1e12:.3f} TFLOP); MHA mode {mqa_us / mha_us:.2f}x faster")
+    return {"workload": "4 prompts x 2048 tokens (= top-k), 128 heads", "mha_us": round(mha_us, 1),
+            "mha_tokens_per_s": round(T / (mha_us * 1e-6), 1), "mha_tflop": round(mha_flop / 1e12, 4),
+            "mha_tflops": round(mha_flop / (mha_us * 1e-6) / 1e12, 1), "mqa_forward_us": round(mqa_us, 1),
+            "mqa_tflop": round(mqa_flop / 1e12, 4), "mha_speedup": round(mqa_us / mha_us, 3)}
 
 
 def bench_quant(lcl, torch, dev, stream, evict, wl):

@@ -164,6 +164,10 @@ DSA_API size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H
  * Long prefills (q_len >= 64 with fp8 inputs) stream the indexer scores
  * through on-chip memory with a running per-row candidate set, so no T x S
  * score matrix is ever written; other shapes score into the workspace first.
+ * When S_max <= topk no row can hold more than topk valid positions, so the
+ * selection is every position ("详解DSA", DSA计算流: the indexer can be
+ * bypassed) and neither the indexer nor the top-k runs; the index inputs are
+ * still validated.
  * ws >= dsa_forward_workspace_size(...) bytes. */
 DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale,
                        const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,

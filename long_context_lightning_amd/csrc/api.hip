@@ -276,10 +276,28 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
   if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
   const ForwardPlan p =
       plan_forward(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype, pages != nullptr);
-  if (!p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
+  const bool keep_all = geom->S_max <= topk;  // no row can have more than topk valid positions
+  if (!keep_all && !p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
   if (ws_bytes < p.total || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(ws);
   const int T = (int)rows_of(geom);
+  if (keep_all) {
+    // "详解DSA", DSA计算流: a sequence no longer than top-k keeps every
+    // position, so the indexer's work is skipped; the selection is 0 .. pos.
+    TopkArgs ta{};
+    ta.B = geom->B;
+    ta.q_len = geom->q_len;
+    ta.S_max = geom->S_max;
+    ta.seq_lens = geom->seq_lens;
+    ta.row_begin = 0;
+    ta.row_count = T;
+    ta.k = topk;
+    ta.idx = idx_out;
+    const hipError_t e = launch_select_all(ta, stream);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+    return hip_status(mla_launches(geom, pages, H, topk, sm_scale, mla_q, mla_dtype, mla_kv, idx_out, out, lse,
+                                   wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream));
+  }
   IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
   ia.pages = page_map(pages);
   hipError_t e = hipSuccess;

@@ -338,6 +338,24 @@ size_t final_lds_bytes(int S_max, int k) {
 }  // namespace
 
 
+// Rows whose valid set fits in k keep every valid position: idx = 0 .. pos,
+// then -1.  Used when S_max <= k, where no score decides anything.
+__global__ __launch_bounds__(256) void k_select_all(TopkArgs a) {
+  const long long n = (long long)a.row_count * a.k;
+  for (long long e = (long long)blockIdx.x * 256 + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+    const int r = (int)(e / a.k), j = (int)(e - (long long)r * a.k);
+    a.idx[e] = j < row_valid_count(a, r) ? j : -1;
+  }
+}
+
+hipError_t launch_select_all(const TopkArgs& a, hipStream_t stream) {
+  const long long n = (long long)a.row_count * a.k;
+  if (n <= 0) return hipSuccess;
+  const long long blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_select_all, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 size_t topk_workspace_bytes(int row_count, int S_max, int k) {
   (void)S_max;
   if (row_count <= 0 || k <= 0) return 0;
