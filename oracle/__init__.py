@@ -26,6 +26,9 @@ the passage of the pages it follows:
   "DSA计算流" and its MLA forward code block; the charlestar page's
   short-prompt paragraph): ``wkv_b`` decompression, causal attention over the
   per-head keys and values.
+* ``kl``: the indexer's KL objective, forward only ("详解DSA" Eq.(3)-(6)):
+  head-summed, L1-normalised attention weights against Softmax(I), on every
+  visible position or on the selected set.
 * ``paged``: paged caches (charlestar page, "Prefill 与 decode 中发生了什么"
   and "Top-k 是算法与 kernel 的交界面"): a block table maps a logical
   position to a page and an offset.
@@ -36,6 +39,7 @@ from .formats import decode_bf16, decode_e4m3fn, e4m3fn_times_512
 from .quant import cache_append, e4m3fn_nearest, quantize_blocks
 from .paged import gather_pages, scatter_pages
 from .mha import decompress as mha_decompress, mha_prefill
+from .kl import attention_lse, indexer_kl
 from .dsa import (
     query_positions,
     indexer_scores,
@@ -60,4 +64,6 @@ __all__ = [
     "scatter_pages",
     "mha_decompress",
     "mha_prefill",
+    "attention_lse",
+    "indexer_kl",
 ]

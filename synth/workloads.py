@@ -14,7 +14,8 @@ Recipe (values are generated in float32 / float64 on the host, then encoded):
 * fp8 configs: indexer q = e4m3fn(N(0,1)) with no scale; indexer k =
   per-token quantised N(0,1) (e4m3fn codes + fp32 scale amax/448); head
   weights w = bf16(N(0,1)/8); MLA q and latent cache = bf16(N(0,1)); for
-  MHA mode, q = bf16(N(0,1)) [T, H, 192] and wkv_b = bf16(N(0,1)/sqrt(512)).
+  MHA mode, q = bf16(N(0,1)) [T, H, 192] and wkv_b = bf16(N(0,1)/sqrt(512));
+  for the KL objective, indexer scores I ~ N(0, 4) float32 [T, S_max].
 * fp32 config ("tiny"): indexer q, k ~ N(0,1)/sqrt(128), w ~ N(0,1), MLA q
   and latent cache ~ N(0,1), all float32, no scales.
 * ``plant``: one template (q*, w*) is drawn; the planted query rows get
@@ -38,7 +39,7 @@ HI, DI, DQK, DV = 64, 128, 576, 512
 ROW_BLOCK = 64
 POS_BLOCK = 4096
 
-_STREAM = {"qi": 1, "w": 2, "ki": 3, "qm": 4, "kv": 5, "plant": 6, "pool": 7, "qh": 8, "wkvb": 9}
+_STREAM = {"qi": 1, "w": 2, "ki": 3, "qm": 4, "kv": 5, "plant": 6, "pool": 7, "qh": 8, "wkvb": 9, "kls": 10}
 D_QH, D_NOPE_V = 192, 256   # MHA mode: q = [nope 128 | rope 64]; wkv_b rows per head = [k_nope 128 | v 128]
 
 
@@ -206,6 +207,12 @@ class Workload:
         g = _rng(self.seed, _STREAM["wkvb"])
         w = _normal32(g, (self.H, D_NOPE_V, DQK - 64)) / np.float32(math.sqrt(DQK - 64))
         return encode_bf16_rne(w) if self.fp8 else w
+
+    def kl_scores(self, rows=None):
+        """Indexer scores standing in for I in the KL objective: [R, S_max]
+        float32 ~ N(0, 4) (the objective reads only visible positions)."""
+        mk = lambda g, n: _normal32(g, (n, self.S_max)) * np.float32(2.0)
+        return self._by_blocks(rows, "kls", mk, (self.S_max,), np.float32)
 
     def _apply_plant(self, rows, out, what):
         p = self._planted()
