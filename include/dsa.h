@@ -315,6 +315,31 @@ DSA_API dsa_status dsa_mha_prefill(const dsa_geom* geom, int32_t H, float sm_sca
                            void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 DSA_API size_t dsa_mha_prefill_workspace_size(int32_t B, int32_t S_max, int32_t H);
 
+/* Indexer KL objective, forward only ("详解DSA" Eq.(3)-(6): the dense
+ * warm-up loss over every visible position, and the sparse-training loss
+ * over the selected set S_t).  For each query row t over its set
+ * (idx == NULL: every s <= pos(t); otherwise the entries 0 <= idx[t,m] <= pos(t),
+ * other values skipped):
+ *   v_s     = sum_h exp(sm_scale * q[t,h,:] . kv[b,s,:] - lse[t,h])   (the heads' attention weights, summed)
+ *   p       = v / sum(v)                                  (Eq.(3): L1-normalised)
+ *   p_hat   = softmax(scores[t, set])                     (Eq.(4))
+ *   kl[t]   = sum_s p_s log(p_s / p_hat_s)                (Eq.(5) / (6); 0 for an empty set)
+ *   *loss   = sum_t kl[t]                                 (if loss != NULL; rows summed in a fixed order)
+ * lse is the attention's per-head natural-log normaliser over the same set
+ * (the lse output of dsa_sparse_mla / dsa_forward for the selected set); any
+ * per-head constant works, since Eq.(3) normalises the sum.
+ *
+ *   q [T, H, 576], kv [B, S_max, 576]: BF16 (the MQA-mode attention inputs)
+ *   lse [T, H] fp32;  scores [T, ld] fp32 (ld >= S_max; only set positions read)
+ *   idx [T, k] int32 or NULL;  kl [T] fp32;  loss: one fp32 or NULL
+ * H a multiple of 32 up to 128; 1 <= k <= 16384 when idx is given.
+ * ws >= dsa_indexer_kl_workspace_size(B, q_len, S_max, idx ? k : 0) bytes. */
+DSA_API dsa_status dsa_indexer_kl(const dsa_geom* geom, int32_t H, float sm_scale,
+                          const void* q, const void* kv, dsa_dtype dtype, const float* lse,
+                          const float* scores, int64_t ld, const int32_t* idx, int32_t k,
+                          float* kl, float* loss, void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_indexer_kl_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t k);
+
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);
 

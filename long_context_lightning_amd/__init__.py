@@ -70,6 +70,8 @@ def load(path=None):
         "dsa_indexer_cache_append_paged": (i32, [gp, pp, vp, i32, vp, vp, vp]),
         "dsa_mha_prefill": (i32, [gp, i32, f32, vp, vp, vp, i32, vp, vp, vp, sz, vp]),
         "dsa_mha_prefill_workspace_size": (sz, [i32, i32, i32]),
+        "dsa_indexer_kl": (i32, [gp, i32, f32, vp, vp, i32, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]),
+        "dsa_indexer_kl_workspace_size": (sz, [i32, i32, i32, i32]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -86,7 +88,8 @@ ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "d
                  "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_indexer_scores_paged",
                  "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
                  "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_mha_prefill",
-                 "dsa_mha_prefill_workspace_size", "dsa_status_string", "dsa_version")
+                 "dsa_mha_prefill_workspace_size", "dsa_indexer_kl", "dsa_indexer_kl_workspace_size",
+                 "dsa_status_string", "dsa_version")
 
 
 def _ptr(t):
@@ -374,3 +377,42 @@ def mha_prefill(geom, q, kv, wkv_b, sm_scale, out=None, lse=None, ws=None, want_
                              _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "dsa_mha_prefill")
     return out, lse
+
+
+def indexer_kl_workspace_size(B, q_len, S_max, k):
+    return int(load().dsa_indexer_kl_workspace_size(B, q_len, S_max, k))
+
+
+def indexer_kl(geom, q, kv, lse, scores, sm_scale, idx=None, kl=None, loss=None, ws=None, stream=None):
+    """dsa_indexer_kl: the indexer's KL objective (forward).  q [T, H, 576] and
+    kv [B, S_max, 576] bf16, lse [T, H] fp32, scores [T, >= S_max] fp32, idx
+    [T, k] int32 or None (every visible position).  Returns (kl [T], loss [1])."""
+    lib = load()
+    T = geom.B * geom.q_len
+    bf = (torch.bfloat16, torch.int16, torch.uint16)
+    _dev(q, "q", bf)
+    _dev(kv, "kv", bf)
+    _dev(lse, "lse", (torch.float32,))
+    _need(q.dim() == 3 and q.shape[0] == T and q.shape[2] == 576, "q must be [T, H, 576]")
+    H = q.shape[1]
+    _need(tuple(kv.shape) == (geom.B, geom.S_max, 576), "kv must be [B, S_max, 576]")
+    _need(tuple(lse.shape) == (T, H), "lse must be [T, H]")
+    _need(scores.is_cuda and scores.dtype == torch.float32 and scores.dim() == 2 and scores.shape[0] == T
+          and scores.stride(1) == 1, "scores must be a row-major fp32 device tensor [T, ld]")
+    k = 0
+    if idx is not None:
+        _dev(idx, "idx", (torch.int32,))
+        _need(idx.dim() == 2 and idx.shape[0] == T, "idx must be [T, k]")
+        k = idx.shape[1]
+    if kl is None:
+        kl = torch.empty((T,), dtype=torch.float32, device=q.device)
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=q.device)
+    need = indexer_kl_workspace_size(geom.B, geom.q_len, geom.S_max, k)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.dsa_indexer_kl(ctypes.byref(geom), H, float(sm_scale), _ptr(q), _ptr(kv), BF16, _ptr(lse), _ptr(scores),
+                            scores.stride(0), _ptr(idx), k, _ptr(kl), _ptr(loss), _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "dsa_indexer_kl")
+    return kl, loss

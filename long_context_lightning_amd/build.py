@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsa.so")
 
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "prefill.hip", "sparse_mla.hip", "quant.hip", "paged.hip", "mha.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "prefill.hip", "sparse_mla.hip", "quant.hip", "paged.hip", "mha.hip", "kl.hip"]
 
 FLAGS = [
     "-O3",

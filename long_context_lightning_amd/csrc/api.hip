@@ -525,6 +525,46 @@ dsa_status dsa_mha_prefill(const dsa_geom* geom, int32_t H, float sm_scale, cons
   return hip_status(launch_mha_prefill(a, stream));
 }
 
+size_t dsa_indexer_kl_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t k) {
+  if (B < 1 || q_len < 1 || S_max < 1) return 0;
+  return kl_workspace_bytes(B * q_len, k > 0 ? k : S_max);
+}
+
+dsa_status dsa_indexer_kl(const dsa_geom* geom, int32_t H, float sm_scale, const void* q, const void* kv,
+                          dsa_dtype dtype, const float* lse, const float* scores, int64_t ld, const int32_t* idx,
+                          int32_t k, float* kl, float* loss, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!geom_ok(geom) || !q || !kv || !lse || !scores || !kl) return DSA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(lse, 4) || !aligned(scores, 4) || !aligned(kl, 4))
+    return DSA_ERR_INVALID_ARG;
+  if ((loss && !aligned(loss, 4)) || (idx && !aligned(idx, 4)) || ld < geom->S_max) return DSA_ERR_INVALID_ARG;
+  if (H < 32 || H > 128 || H % 32 != 0) return DSA_ERR_INVALID_ARG;
+  if (idx && (k < 1 || k > kMaxMlaK)) return DSA_ERR_INVALID_ARG;
+  if (dtype != DSA_BF16) return DSA_ERR_UNSUPPORTED;
+  const int kk = idx ? k : geom->S_max;
+  const size_t need = dsa_indexer_kl_workspace_size(geom->B, geom->q_len, geom->S_max, idx ? k : 0);
+  if (ws_bytes < need || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+  KlArgs a;
+  a.B = geom->B;
+  a.q_len = geom->q_len;
+  a.S_max = geom->S_max;
+  a.H = H;
+  a.k = kk;
+  a.seq_lens = geom->seq_lens;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.kv = kv;
+  a.lse = lse;
+  a.scores = scores;
+  a.ld = ld;
+  a.idx = idx;
+  a.kl = kl;
+  a.loss = loss;
+  a.ws = static_cast<float*>(ws);
+  a.row_begin = 0;
+  a.row_count = (int)rows_of(geom);
+  return hip_status(launch_indexer_kl(a, stream));
+}
+
 const char* dsa_status_string(dsa_status s) {
   switch (s) {
     case DSA_OK: return "DSA_OK";

@@ -284,4 +284,24 @@ struct MhaArgs {
 size_t mha_workspace_bytes(int B, int S_max, int H);
 hipError_t launch_mha_prefill(const MhaArgs& a, hipStream_t s);
 
+// Indexer KL objective (forward): per-row KL of the head-summed, normalised
+// attention weights against Softmax(I) over a set of positions.
+struct KlArgs {
+  int B, q_len, S_max, H, k;  // k: entries per row (idx width, or S_max for every position)
+  const int32_t* seq_lens;
+  float sm_scale;
+  const void* q;          // [T,H,576] bf16
+  const void* kv;         // [B,S_max,576] bf16
+  const float* lse;       // [T,H] natural log
+  const float* scores;    // [T, ld] indexer scores I
+  long long ld;
+  const int32_t* idx;     // [T,k] or null (the set is 0 .. pos)
+  float* kl;              // [row_count]
+  float* loss;            // scalar or null
+  float* ws;              // per-split partials
+  int row_begin, row_count;
+};
+size_t kl_workspace_bytes(int rows, int k);
+hipError_t launch_indexer_kl(const KlArgs& a, hipStream_t s);
+
 }  // namespace dsa

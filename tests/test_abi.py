@@ -185,3 +185,20 @@ def test_mha_prefill_validation():
     assert lib.dsa_mha_prefill(ctypes.byref(g), 16, 0.1, P(FAKE + 8), P(FAKE), P(FAKE), 1, P(FAKE), None, P(FAKE),
                                need, None) == 1
     assert lib.dsa_mha_prefill_workspace_size(0, 64, 16) == 0
+
+
+def test_indexer_kl_validation():
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=1, S=256)
+    need = lib.dsa_indexer_kl_workspace_size(2, 1, 256, 64)
+    assert need > 0
+    call = lambda H, dt, ld, idx, k, wsb: lib.dsa_indexer_kl(ctypes.byref(g), H, 0.1, P(FAKE), P(FAKE), dt, P(FAKE),
+                                                             P(FAKE), ld, idx, k, P(FAKE), None, P(FAKE), wsb, None)
+    assert call(128, 0, 256, P(FAKE), 64, need) == 2     # bf16 only
+    assert call(48, 1, 256, P(FAKE), 64, need) == 1      # H a multiple of 32
+    assert call(256, 1, 256, P(FAKE), 64, need) == 1
+    assert call(128, 1, 255, P(FAKE), 64, need) == 1     # ld < S_max
+    assert call(128, 1, 256, P(FAKE), 0, need) == 1      # k = 0 with idx
+    assert call(128, 1, 256, P(FAKE), 64, need - 1) == 3
+    assert lib.dsa_indexer_kl_workspace_size(2, 1, 256, 0) > 0   # dense: the set is every position
