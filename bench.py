@@ -200,6 +200,9 @@ def main():
     # ------------------------------------ short prefill: MHA mode vs MQA mode
     mha = bench_mha(lcl, torch, dev, stream, evict)
 
+    # ------------------------------------------------ indexer KL objective
+    kl = bench_kl(lcl, torch, dev, stream, evict)
+
     # --------------------------------------------------------- prefill 64K
     prefill = None
     if not args.no_prefill:
@@ -234,6 +237,7 @@ def main():
         "quantize": quant,
         "paged": paged,
         "mha_prefill": mha,
+        "indexer_kl": kl,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
@@ -361,6 +365,55 @@ def bench_mha(lcl, torch, dev, stream, evict, steps=5):
             "mha_tokens_per_s": round(T / (mha_us * 1e-6), 1), "mha_tflop": round(mha_flop / 1e12, 4),
             "mha_tflops": round(mha_flop / (mha_us * 1e-6) / 1e12, 1), "mqa_forward_us": round(mqa_us, 1),
             "mqa_tflop": round(mqa_flop / 1e12, 4), "mha_speedup": round(mqa_us / mha_us, 3)}
+
+
+def bench_kl(lcl, torch, dev, stream, evict, steps=5):
+    """The indexer's KL objective over the selected sets (Eq.(6)) for an
+    8192-token prefill: 8192 query rows x top-2048 sets (selected by dsa_topk
+    from the scores), 128 heads.  Inputs drawn on the GPU with torch's seeded
+    generator: MLA queries and latent cache ~ N(0,1) bf16, indexer scores
+    ~ N(0,4) fp32 (causally masked), per-head lse ~ 5 + N(0,1).  Timed per
+    call after a last-level cache eviction (mean of `steps`)."""
+    L, k, H = 8192, 2048, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(9)
+    qm = torch.randn((L, H, 576), generator=g, device=dev).to(torch.bfloat16)
+    kv = torch.randn((1, L, 576), generator=g, device=dev).to(torch.bfloat16)
+    sc = torch.randn((L, L), generator=g, device=dev) * 2.0
+    sc = torch.where(torch.arange(L, device=dev)[None, :] <= torch.arange(L, device=dev)[:, None], sc,
+                     torch.tensor(float("-inf"), device=dev)).contiguous()
+    lse = 5.0 + torch.randn((L, H), generator=g, device=dev)
+    seq = torch.tensor([L], dtype=torch.int32, device=dev)
+    geom = lcl.make_geom(1, L, L, seq)
+    idx = lcl.topk(geom, sc, k)
+    kl = torch.empty((L,), dtype=torch.float32, device=dev)
+    loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(lcl.indexer_kl_workspace_size(1, L, L, k), 256), dtype=torch.uint8, device=dev)
+    sm = 1.0 / math.sqrt(192.0)
+
+    def call():
+        lcl.indexer_kl(geom, qm, kv, lse, sc, sm, idx=idx, kl=kl, loss=loss, ws=ws)
+
+    call()
+    ts = []
+    for _ in range(steps):
+        evict()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]) * 1e3)
+    us = sum(ts) / len(ts)
+    entries = float((idx >= 0).sum().item())
+    flop = entries * H * 576 * 2
+    log(f"indexer KL (Eq.6) 8192 rows x top-{k}, {H} heads: {us:.1f} us, {flop / 1e12:.3f} TFLOP -> "
+        f"{flop / (us * 1e-6) / 1e12:.1f} TFLOP/s ({flop / (us * 1e-6) / 2.5e15:.1%} of bf16 peak)")
+    del qm, kv, sc, lse, idx, kl, loss, ws
+    torch.cuda.empty_cache()
+    return {"workload": "8192-token prefill, top-2048 sets, 128 heads", "us": round(us, 1),
+            "tflop": round(flop / 1e12, 4), "tflops": round(flop / (us * 1e-6) / 1e12, 1),
+            "mfma_frac": round(flop / (us * 1e-6) / 2.5e15, 4)}
 
 
 def bench_quant(lcl, torch, dev, stream, evict, wl):
