@@ -14,8 +14,9 @@
 // Two kernels:
 //
 // k_mha_decompress: [k_nope | v] = latent . wkv_b^T per head, a bf16 GEMM on
-//   v_mfma_f32_16x16x32_bf16.  A block computes 128 positions x one 128-wide
-//   half (k_nope or v) of one head; 4 waves of 64 x 64.  64-deep K chunks of
+//   v_mfma_f32_16x16x32_bf16.  A block computes 256 positions x the 256
+//   output columns of one head (k_nope and v); 8 waves of 64 columns x 128
+//   positions, so each copy instruction feeds 8 MFMAs.  64-deep K chunks of
 //   both operands go global -> LDS by DMA (double buffered), 16-byte pieces
 //   XOR-swizzled so the 16 rows one fragment read covers fall on distinct
 //   banks.  Output head-major: k_nope[b][h][s][128], v[b][h][s][128] bf16.
@@ -72,61 +73,62 @@ __device__ __forceinline__ uint2 pack4_bf16(float x0, float x1, float x2, float 
 
 // ------------------------------------------------------------ decompression
 
-constexpr int kGT = 128;                 // positions (and output columns) per block
+constexpr int kGT = 256;                 // positions per block
+constexpr int kGN = 2 * kDVh;            // output columns per block: one head's k_nope and v rows
 constexpr int kGK = 64;                  // K depth per stage
 constexpr int kGRow = 2 * kGK;           // bytes of one row of a stage (128)
-constexpr int kGOp = kGT * kGRow;        // one operand's stage (16 KB)
-constexpr int kGStage = 2 * kGOp;        // W and latent
+constexpr int kGW = kGN * kGRow;         // W part of a stage (32 KB)
+constexpr int kGX = kGT * kGRow;         // latent part of a stage (32 KB)
+constexpr int kGStage = kGW + kGX;
 constexpr int kGSteps = kDL / kGK;       // 8
-constexpr int kGDma = 2 * kGOp / 1024 / 4;  // DMA instructions per wave per stage (8)
+constexpr int kGWaves = 8;
+constexpr int kGDma = kGStage / 1024 / kGWaves;  // DMA instructions per wave per stage (8)
 
-// Stage kc of the block's operands: W rows (output columns) then latent rows
-// (positions), 128 bytes per row; lane l of instruction i fills 16-byte slot
-// 64i + l, i.e. row r = slot / 8, stored piece p = slot % 8, which holds the
-// row's logical piece p ^ ((r >> 1) & 7).
-__device__ __forceinline__ void gemm_stage(const MhaArgs& a, int b, int h, int half, int s0, int L, int kc,
-                                           uint32_t stage_off, int wave, int lane) {
+// Stage kc of the block's operands: the head's 256 W rows (output columns)
+// then 256 latent rows (positions), 128 bytes per row; lane l of instruction
+// i fills 16-byte slot 64i + l of its part, i.e. row r = slot / 8, stored
+// piece p = slot % 8, which holds the row's logical piece p ^ ((r >> 1) & 7).
+__device__ __forceinline__ void gemm_stage(const MhaArgs& a, int b, int h, int s0, int L, int kc, uint32_t stage_off,
+                                           int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < kGDma; ++u) {
-    const int i = wave * kGDma + u;          // 0..31: 0..15 W, 16..31 latent
-    const int slot = 64 * (i & 15) + lane;
+    const int i = wave * kGDma + u;          // 0..63: 0..31 W, 32..63 latent
+    const int slot = 64 * (i & 31) + lane;
     const int r = slot >> 3, p = slot & 7;
     const int piece = p ^ ((r >> 1) & 7);
     const char* src;
-    if (i < 16) {
-      src = reinterpret_cast<const char*>(a.wkv_b) +
-            (((size_t)h * 2 * kDVh + (size_t)half * kDVh + r) * kDL + (size_t)kc * kGK + 8 * piece) * 2;
+    if (i < 32) {
+      src = reinterpret_cast<const char*>(a.wkv_b) + (((size_t)h * kGN + r) * kDL + (size_t)kc * kGK + 8 * piece) * 2;
     } else {
       const int s = min(s0 + r, L - 1);
-      src = reinterpret_cast<const char*>(a.kv) +
-            (((size_t)b * a.S_max + s) * kDQK + (size_t)kc * kGK + 8 * piece) * 2;
+      src = reinterpret_cast<const char*>(a.kv) + (((size_t)b * a.S_max + s) * kDQK + (size_t)kc * kGK + 8 * piece) * 2;
     }
-    dma16_lds_at(src, stage_off + (i < 16 ? 0 : kGOp) + 1024 * (i & 15));
+    dma16_lds_at(src, stage_off + (i < 32 ? 0 : kGW) + 1024 * (i & 31));
   }
 }
 
-__global__ __launch_bounds__(256, 2) void k_mha_decompress(MhaArgs a) {
+__global__ __launch_bounds__(kGWaves * 64, 1) void k_mha_decompress(MhaArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kGStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int b = blockIdx.z, h = blockIdx.y >> 1, half = blockIdx.y & 1;
+  const int b = blockIdx.z, h = blockIdx.y;
   const int L = clamped_len(a.seq_lens, b, a.S_max);
   const int s0 = blockIdx.x * kGT;
   if (s0 >= L) return;
   const uint32_t base = lds_offset(lds);
-  const int wn = wave & 1, wsb = wave >> 1;  // 64-column block, 64-position block
+  const int wn = wave & 3, wsb = wave >> 2;  // 64-column block, 128-position block
 
-  v4f acc[4][4];
+  v4f acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  gemm_stage(a, b, h, half, s0, L, 0, base, wave, lane);
+  gemm_stage(a, b, h, s0, L, 0, base, wave, lane);
   for (int kc = 0; kc < kGSteps; ++kc) {
     if (kc + 1 < kGSteps) {
-      gemm_stage(a, b, h, half, s0, L, kc + 1, base + ((kc + 1) & 1) * kGStage, wave, lane);
+      gemm_stage(a, b, h, s0, L, kc + 1, base + ((kc + 1) & 1) * kGStage, wave, lane);
       vm_wait<kGDma>();
     } else {
       vm_wait<0>();
@@ -135,33 +137,38 @@ __global__ __launch_bounds__(256, 2) void k_mha_decompress(MhaArgs a) {
     const unsigned char* st = lds + (kc & 1) * kGStage;
 #pragma unroll
     for (int kk = 0; kk < kGK / 32; ++kk) {
-      v8bf wf[4], xf[4];
+      const int pc = 4 * kk + g;  // logical piece
+      v8bf wf[4], xf[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rw = 64 * wn + 16 * j + c;   // output column (W row)
-        const int rx = 64 * wsb + 16 * j + c;  // position (latent row)
-        const int pc = 4 * kk + g;             // logical piece
-        wf[j] = as_v8bf(*reinterpret_cast<const v4i*>(st + rw * kGRow + 16 * (pc ^ ((rw >> 1) & 7))));
-        xf[j] = as_v8bf(*reinterpret_cast<const v4i*>(st + kGOp + rx * kGRow + 16 * (pc ^ ((rx >> 1) & 7))));
+      for (int i = 0; i < 4; ++i) {
+        const int rw = 64 * wn + 16 * i + c;  // output column (W row)
+        wf[i] = as_v8bf(*reinterpret_cast<const v4i*>(st + rw * kGRow + 16 * (pc ^ ((rw >> 1) & 7))));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int rx = 128 * wsb + 16 * j + c;  // position (latent row)
+        xf[j] = as_v8bf(*reinterpret_cast<const v4i*>(st + kGW + rx * kGRow + 16 * (pc ^ ((rx >> 1) & 7))));
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16(wf[i], xf[j], acc[i][j]);
     }
     lds_barrier();  // the next step refills this stage
   }
-  // D[column 4g + i][position c] of block (i, j): four consecutive columns of
-  // one position per lane -> one 8-byte store.
-  uint16_t* dst = static_cast<uint16_t*>(half ? a.v_ws : a.knope_ws) + ((size_t)b * a.H + h) * a.S_max * kDVh;
+  // D[column 4g + i'][position c] of block (i, j): four consecutive columns of
+  // one position per lane -> one 8-byte store; columns 0..127 are k_nope,
+  // 128..255 are v.
+  uint16_t* dst = static_cast<uint16_t*>(wn < 2 ? a.knope_ws : a.v_ws) + ((size_t)b * a.H + h) * a.S_max * kDVh;
+  const int col0 = 64 * (wn & 1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int s = s0 + 64 * wsb + 16 * j + c;
+  for (int j = 0; j < 8; ++j) {
+    const int s = s0 + 128 * wsb + 16 * j + c;
     if (s >= L) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint2 pk = pack4_bf16(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(dst + (size_t)s * kDVh + 64 * wn + 16 * i + 4 * g) = pk;
+      *reinterpret_cast<uint2*>(dst + (size_t)s * kDVh + col0 + 16 * i + 4 * g) = pk;
     }
   }
 }
@@ -397,8 +404,8 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
 size_t mha_workspace_bytes(int B, int S_max, int H) { return (size_t)2 * B * H * S_max * kDVh * sizeof(uint16_t); }
 
 hipError_t launch_mha_prefill(const MhaArgs& a, hipStream_t stream) {
-  const dim3 g1((unsigned)((a.S_max + kGT - 1) / kGT), (unsigned)(2 * a.H), (unsigned)a.B);
-  hipLaunchKernelGGL(k_mha_decompress, g1, dim3(256), 0, stream, a);
+  const dim3 g1((unsigned)((a.S_max + kGT - 1) / kGT), (unsigned)a.H, (unsigned)a.B);
+  hipLaunchKernelGGL(k_mha_decompress, g1, dim3(kGWaves * 64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 g2((unsigned)((a.q_len + kAQ - 1) / kAQ), (unsigned)a.H, (unsigned)a.B);
