@@ -305,20 +305,31 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
     if (s0 > w_maxpos) continue;  // every key of the tile is past this wave's queries
     const unsigned char* kt = ring + (n % kASlots) * kAStage;
 
-    // scores S^T[key 16 kb + 4g + i][query 16 qb + c]
+    // scores S^T[key 16 kb + 4g + i][query 16 qb + c]; the four K fragments
+    // of k-step ks + 1 are read while the MFMAs of k-step ks run
     v4f sa[4][2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) sa[kb][0] = sa[kb][1] = v4f{0.f, 0.f, 0.f, 0.f};
+    v8bf kf[2][4];
+    auto kread = [&](int ks, v8bf (&dst)[4]) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        dst[kb] = as_v8bf(*reinterpret_cast<const v4i*>(kt + ((ks & 1) ? kbase1 : kbase0) + 16 * kKRow * kb +
+                                                         128 * (ks >> 1)));
+    };
+    kread(0, kf[0]);
 #pragma unroll
     for (int ks = 0; ks < kDQh / 32; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + 1 < kDQh / 32) kread(ks + 1, kf[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const unsigned char* p = kt + ((ks & 1) ? kbase1 : kbase0) + 16 * kKRow * kb + 128 * (ks >> 1);
-        const v8bf kf = as_v8bf(*reinterpret_cast<const v4i*>(p));
-        sa[kb][0] = mfma_bf16(kf, qf[0][ks], sa[kb][0]);
-        sa[kb][1] = mfma_bf16(kf, qf[1][ks], sa[kb][1]);
+        sa[kb][0] = mfma_bf16(kf[ks & 1][kb], qf[0][ks], sa[kb][0]);
+        sa[kb][1] = mfma_bf16(kf[ks & 1][kb], qf[1][ks], sa[kb][1]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (s0 + kAK - 1 > w_minpos) {  // diagonal tile: keys past a query's position are -inf
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -366,19 +377,29 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
 
     // values: the V^T fragment (16 dims x the 32 keys of step kk) feeds both
     // query blocks
+    // V^T fragments are read two value blocks ahead of their MFMAs
     const unsigned char* vt = kt + vbase;
+    constexpr int kVSteps = 2 * (kDVh / 16);  // (kk, db) pairs
+    constexpr int kVAhead = 2;
+    v4s vlo[kVAhead + 1], vhi[kVAhead + 1];
+    auto vread = [&](int j) {
+      const unsigned char* p0 = vt + 32 * (j / (kDVh / 16)) * kVRow + 32 * (j % (kDVh / 16));
+      vlo[j % (kVAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+      vhi[j % (kVAhead + 1)] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 16 * kVRow));
+    };
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int j = 0; j < kVAhead; ++j) vread(j);
 #pragma unroll
-      for (int db = 0; db < kDVh / 16; ++db) {
-        const unsigned char* p0 = vt + 32 * kk * kVRow + 32 * db;
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + 16 * kVRow));
-        const v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db][0] = mfma_bf16(vf, pf[kk][0], acc[db][0]);
-        acc[db][1] = mfma_bf16(vf, pf[kk][1], acc[db][1]);
-      }
+    for (int j = 0; j < kVSteps; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + kVAhead < kVSteps) vread(j + kVAhead);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kk = j / (kDVh / 16), db = j % (kDVh / 16), sl = j % (kVAhead + 1);
+      const v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(vlo[sl], vhi[sl], 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[db][0] = mfma_bf16(vf, pf[kk][0], acc[db][0]);
+      acc[db][1] = mfma_bf16(vf, pf[kk][1], acc[db][1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // out[t, h, dims 16 db + 4g .. +3] for query c of block qb; lse by the g = 0 lanes
