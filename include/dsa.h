@@ -159,7 +159,9 @@ DSA_API size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H
 /* The whole forward path: indexer -> top-k -> sparse MLA, on one stream.
  * Arguments as in the three calls above (index_* = the indexer inputs,
  * mla_* = the attention inputs, both at the same geometry).  idx_out
- * [T, topk] int32 receives the selection (ascending, -1 padded).
+ * [T, topk] int32 receives the selection (ascending, -1 padded); it may be
+ * NULL, and the selection then lives in the workspace, which must hold
+ * T * topk * 4 bytes (rounded up to 256) beyond the size query's value.
  *
  * Long prefills (q_len >= 64 with fp8 inputs) stream the indexer scores
  * through on-chip memory with a running per-row candidate set, so no T x S

@@ -270,13 +270,17 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
             index_q_scale=None, idx=None, out=None, lse=None, ws=None, want_lse=True, stream=None, pages=None):
     """dsa_forward: indexer -> top-k -> sparse MLA (dsa_forward_paged when
     ``pages`` is given, with ``index_k``, ``index_k_scale`` and ``mla_kv`` the
-    page pools).  Returns (idx, out, lse)."""
+    page pools).  ``idx=False`` passes idx_out = NULL (the selection stays in
+    the workspace and None is returned for it).  Returns (idx, out, lse)."""
     lib = load()
     T = geom.B * geom.q_len
     H = mla_q.shape[1]
     dev = mla_q.device
+    no_idx = idx is False
     if idx is None:
         idx = torch.empty((T, topk_k), dtype=torch.int32, device=dev)
+    elif no_idx:
+        idx = None
     if out is None:
         out = torch.empty((T, H, 512), dtype=mla_q.dtype, device=dev)
     if lse is None and want_lse:
@@ -284,11 +288,14 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
     idt, mdt = _index_dtype(index_q), _mla_dtype(mla_q)
     size_fn = forward_workspace_size if pages is None else forward_paged_workspace_size
     need = size_fn(geom.B, geom.q_len, geom.S_max, H, topk_k, idt, mdt)
+    if no_idx:
+        need += (T * topk_k * 4 + 255) // 256 * 256
     if ws is None:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     for name, t in (("index_q", index_q), ("index_w", index_w), ("index_k", index_k), ("mla_q", mla_q),
                     ("mla_kv", mla_kv), ("idx", idx), ("out", out)):
-        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+        if t is not None:
+            _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
     _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == _cache_shape(geom, pages, (128,)),
           "indexer shapes mismatch")
     _need(tuple(mla_kv.shape) == _cache_shape(geom, pages, (576,)) and mla_q.shape[0] == T, "MLA shapes mismatch")

@@ -270,17 +270,21 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
   dsa_status st = check_indexer_inputs(geom, index_q, index_dtype, index_q_scale, index_w, index_w_dtype, index_k,
                                        index_dtype, index_k_scale);
   if (st != DSA_OK) return st;
-  if (!idx_out || !aligned(idx_out, 4) || topk < 1) return DSA_ERR_INVALID_ARG;
-  st = check_mla(geom, H, topk, mla_q, mla_dtype, mla_kv, idx_out, out, lse);
+  if ((idx_out && !aligned(idx_out, 4)) || topk < 1) return DSA_ERR_INVALID_ARG;
+  // any non-null placeholder for the MLA check; the real selection buffer is
+  // idx_out or the workspace tail
+  st = check_mla(geom, H, topk, mla_q, mla_dtype, mla_kv, idx_out ? idx_out : static_cast<int32_t*>(ws), out, lse);
   if (st != DSA_OK) return st;
   if (pages && !pages_ok(geom, pages)) return DSA_ERR_INVALID_ARG;
   const ForwardPlan p =
       plan_forward(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype, pages != nullptr);
   const bool keep_all = geom->S_max <= topk;  // no row can have more than topk valid positions
   if (!keep_all && !p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
-  if (ws_bytes < p.total || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
-  char* wsb = static_cast<char*>(ws);
   const int T = (int)rows_of(geom);
+  const size_t need = p.total + (idx_out ? 0 : align_up((size_t)T * topk * sizeof(int32_t)));
+  if (ws_bytes < need || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
+  char* wsb = static_cast<char*>(ws);
+  if (!idx_out) idx_out = reinterpret_cast<int32_t*>(wsb + p.total);  // selection kept in the workspace
   if (keep_all) {
     // "详解DSA", DSA计算流: a sequence no longer than top-k keeps every
     // position, so the indexer's work is skipped; the selection is 0 .. pos.

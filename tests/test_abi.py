@@ -202,3 +202,14 @@ def test_indexer_kl_validation():
     assert call(128, 1, 256, P(FAKE), 0, need) == 1      # k = 0 with idx
     assert call(128, 1, 256, P(FAKE), 64, need - 1) == 3
     assert lib.dsa_indexer_kl_workspace_size(2, 1, 256, 0) > 0   # dense: the set is every position
+
+
+def test_forward_without_idx_out_needs_the_selection_in_the_workspace():
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=1, S=4096)
+    need = lib.dsa_forward_workspace_size(2, 1, 4096, 128, 512, 2, 1)
+    call = lambda wsb: lib.dsa_forward(ctypes.byref(g), 512, 128, 0.1, P(FAKE), 2, None, P(FAKE), 1, P(FAKE), None,
+                                       P(FAKE), P(FAKE), 1, None, P(FAKE), None, P(FAKE), wsb, None)
+    assert call(need) == 3                          # the 2 x 512 selection does not fit
+    assert call(need + 2 * 512 * 4 - 1) == 3

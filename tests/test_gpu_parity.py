@@ -216,3 +216,22 @@ def test_full_prefill64k_sampled(dsa_gpu):
     check_topk(gi, ref, wl.positions()[sample], k)
     check_attention(from_dev(out[torch.from_numpy(sample).cuda()]), lse.cpu().numpy()[sample], up,
                     gi.astype(np.int64), sample)
+
+
+def test_forward_without_idx_out(dsa_gpu):
+    """idx_out = NULL keeps the selection in the workspace; the attention
+    output is bit-identical to the call that returns the selection (decode
+    with a materialised score buffer, and a streamed prefill)."""
+    for name, B, q_len, seq, S, k, H in (("noidx_decode", 3, 2, [5000, 3001, 4097], 5000, 512, 32),
+                                         ("noidx_prefill", 1, 600, [600], 600, 128, 16)):
+        _say(f"[forward] {name}: idx_out NULL")
+        wl = make_workload(name, B, q_len, seq, S, k, H, seed=15)
+        up = Uploaded(wl)
+        g = up.geom(dsa_gpu)
+        idx, out, lse = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                        index_k_scale=up.d_ks)
+        none, out2, lse2 = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                           index_k_scale=up.d_ks, idx=False)
+        torch.cuda.synchronize()
+        assert none is None
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
