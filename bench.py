@@ -206,11 +206,20 @@ def main():
     # ------------------------------------------------ indexer KL objective
     kl = bench_kl(lcl, torch, dev, stream, evict)
 
+    # ---------------------------- the other decode and prefill configurations
+    del d, idx, out, lse, ws, tk_ws, mla_ws
+    torch.cuda.empty_cache()
+    other = {
+        "decode32k": bench_forward_config(lcl, torch, dev, stream, evict, "decode32k: 64 seqs x 1 query, ctx 32768",
+                                          B=64, q_len=1, S=32768, k=2048, H=128, steps=args.steps, unit="queries/s"),
+        "prefill8k": bench_forward_config(lcl, torch, dev, stream, evict, "prefill8k: 1 x 8192 causal",
+                                          B=1, q_len=8192, S=8192, k=2048, H=128, steps=max(3, args.steps // 4),
+                                          unit="tokens/s"),
+    }
+
     # --------------------------------------------------------- prefill 64K
     prefill = None
     if not args.no_prefill:
-        del d, idx, out, lse, ws, tk_ws, mla_ws
-        torch.cuda.empty_cache()
         prefill = bench_prefill(args, lcl, torch, np, dev, stream, evict)
 
     # ------------------------------------------------------ CPU baseline
@@ -241,6 +250,7 @@ def main():
         "paged": paged,
         "mha_prefill": mha,
         "indexer_kl": kl,
+        "other_configs": other,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
@@ -368,6 +378,62 @@ def bench_mha(lcl, torch, dev, stream, evict, steps=5):
             "mha_tokens_per_s": round(T / (mha_us * 1e-6), 1), "mha_tflop": round(mha_flop / 1e12, 4),
             "mha_tflops": round(mha_flop / (mha_us * 1e-6) / 1e12, 1), "mqa_forward_us": round(mqa_us, 1),
             "mqa_tflop": round(mqa_flop / 1e12, 4), "mha_speedup": round(mqa_us / mha_us, 3)}
+
+
+def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, H, steps, unit):
+    """dsa_forward on another of the five configurations, inputs drawn on the
+    GPU with torch's seeded generator following the decode recipe (indexer q
+    and k ~ N(0,1) -> e4m3, k with per-token amax/448 scales, w ~ N(0,1)/8
+    bf16, MLA q and latent cache ~ N(0,1) bf16; full cache lengths).  Two
+    warm-up steps, then the mean of `steps`, each after the cache scrub.
+    Returns the rate in queries/s (decode) or tokens/s (prefill)."""
+    T = B * q_len
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    qi = torch.randn((T, 64, 128), generator=g, device=dev).to(torch.float8_e4m3fn)
+    ki = torch.empty((B, S, 128), dtype=torch.float8_e4m3fn, device=dev)
+    ks = torch.empty((B, S), dtype=torch.float32, device=dev)
+    for b in range(B):
+        kf = torch.randn((S, 128), generator=g, device=dev)
+        ks[b] = (kf.abs().amax(dim=-1).clamp_min(2.0 ** -126) / 448.0).float()
+        ki[b] = (kf / ks[b][:, None]).to(torch.float8_e4m3fn)
+    w = (torch.randn((T, 64), generator=g, device=dev) / 8).to(torch.bfloat16)
+    qm = torch.empty((T, H, 576), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, T, 4096):
+        qm[r0:r0 + 4096] = torch.randn((min(4096, T - r0), H, 576), generator=g, device=dev).to(torch.bfloat16)
+    kv = torch.empty((B, S, 576), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        kv[b] = torch.randn((S, 576), generator=g, device=dev).to(torch.bfloat16)
+    seq = torch.full((B,), S, dtype=torch.int32, device=dev)
+    geom = lcl.make_geom(B, q_len, S, seq)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(lcl.forward_workspace_size(B, q_len, S, H, k, lcl.FP8_E4M3FN, lcl.BF16), dtype=torch.uint8,
+                     device=dev)
+    sm = 1.0 / math.sqrt(192.0)
+
+    def fwd():
+        lcl.forward(geom, k, sm, qi, w, ki, qm, kv, index_k_scale=ks, idx=idx, out=out, ws=ws, want_lse=False)
+
+    for _ in range(2):
+        evict()
+        fwd()
+    ts = []
+    for _ in range(steps):
+        evict()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ts.append(e[0].elapsed_time(e[1]))
+    ms = sum(ts) / len(ts)
+    rate = T / (ms * 1e-3)
+    log(f"{label}: {ms * 1e3:.1f} us/step -> {rate:,.0f} {unit}")
+    del qi, ki, ks, w, qm, kv, idx, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": label, "us_per_step": round(ms * 1e3, 2), "value": round(rate, 1), "unit": unit,
+            "steps": steps}
 
 
 def bench_kl(lcl, torch, dev, stream, evict, steps=5):
