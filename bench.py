@@ -253,6 +253,7 @@ def main():
         "other_configs": other,
         "prefill": prefill,
         "cpu_baseline": cpu,
+        "system": system_info(torch, lcl),
     }
     print(json.dumps(line), flush=True)
 
@@ -378,6 +379,14 @@ def bench_mha(lcl, torch, dev, stream, evict, steps=5):
             "mha_tokens_per_s": round(T / (mha_us * 1e-6), 1), "mha_tflop": round(mha_flop / 1e12, 4),
             "mha_tflops": round(mha_flop / (mha_us * 1e-6) / 1e12, 1), "mqa_forward_us": round(mqa_us, 1),
             "mqa_tflop": round(mqa_flop / 1e12, 4), "mha_speedup": round(mqa_us / mha_us, 3)}
+
+
+def system_info(torch, lcl):
+    """Versions and target of the run: HIP runtime, torch, device and gfx
+    architecture, library version."""
+    props = torch.cuda.get_device_properties(0)
+    return {"device": props.name, "gfx": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "hip": torch.version.hip, "torch": torch.__version__, "libdsa": lcl.load().dsa_version().decode()}
 
 
 def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, H, steps, unit):
