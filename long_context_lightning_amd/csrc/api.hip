@@ -331,8 +331,10 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
       ia.row_count = rc;
       ia.scores = scores;
       ia.ld = geom->S_max;
-      topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
-      ia.zero_rows = rc;
+      if (!topk_row_fused(geom->S_max, topk)) {  // the multi-launch top-k counts into cleared counters
+        topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
+        ia.zero_rows = rc;
+      }
       e = run_indexer(ia, fp8, stream);
       if (e != hipSuccess) break;
       e = run_topk(ta, stream);

@@ -238,6 +238,8 @@ size_t topk_workspace_bytes(int row_count, int S_max, int k);
 // The words of a top-k workspace that must be zero before launch_topk.
 void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* stride_words, int* words);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+// launch_topk selects each row in one block (no workspace use) for these sizes.
+bool topk_row_fused(int S_max, int k);
 // Every valid position (0 .. pos, then -1) for rows whose valid set fits in k.
 hipError_t launch_select_all(const TopkArgs& a, hipStream_t s);
 

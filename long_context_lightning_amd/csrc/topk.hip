@@ -185,42 +185,39 @@ __global__ __launch_bounds__(kSegThreads) void k_topk_gather(TopkArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+// Exact selection of row r (n > k valid positions) from its 12-bit histogram
+// hist12 and its candidate list (ekey, eidx: cnt_in entries, the keys and
+// positions of every score in the bins at or above the threshold bin,
+// unless that set exceeds cap_for(k), in which case the row is selected
+// straight from the scores).  region: the LDS layout of final_lds_bytes.
+// Called by all kFinThreads threads of the block.
+__device__ void select_row(const TopkArgs& a, int r, int n, int32_t* out, const uint32_t* hist12,
+                           const uint32_t* ekey, const uint32_t* eidx, uint32_t cnt_in, uint32_t* region) {
   constexpr int NW = kFinThreads / 64;
   constexpr int kCPer = kCapMax / kFinThreads;        // candidates per thread at most
   static_assert(kFinThreads == 1 << kFinDigit, "one digit bin per thread");
   const int Wmax = (((a.S_max + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
-  uint32_t* bitmap = dyn;                              // positions kept (16-byte aligned)
+  uint32_t* bitmap = region;                           // positions kept (16-byte aligned)
   uint32_t* tbits = bitmap + Wmax;                     // copies of tau, when ties need the position rule
   uint32_t* hist = tbits + Wmax;                       // 1 << kFinDigit (16-byte aligned)
   uint32_t* whist = hist + (1 << kFinDigit);           // NW << kDigitBits (score-row path)
   uint32_t* sm = whist + (NW << kDigitBits);           // 64
-
-  const int r = blockIdx.x;
-  const int n = row_valid_count(a, r);
-  int32_t* out = a.idx + (long long)r * a.k;
   const int tid = threadIdx.x;
-  if (n <= a.k) {
-    for (int j = tid; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
-    return;
-  }
-  RowWs w = row_ws(a.ws, r, a.k);
   // The candidate list goes to registers first (its length is the gather
   // launch's count), so the loads overlap the threshold search.
   const uint32_t cap = (uint32_t)cap_for(a.k);
-  const uint32_t cnt = min(w.meta[0], cap);
+  const uint32_t cnt = min(cnt_in, cap);
   uint32_t ck[kCPer], cp[kCPer];
 #pragma unroll
   for (int j = 0; j < kCPer; ++j) {
     const uint32_t i = (uint32_t)(tid + j * kFinThreads);
     const uint32_t ic = i < cnt ? i : (cnt ? cnt - 1 : 0u);
-    ck[j] = w.ekey[ic];
-    cp[j] = w.eidx[ic];
+    ck[j] = ekey[ic];
+    cp[j] = eidx[ic];
   }
   uint32_t bstar, above;
-  find_threshold_bin<kFinThreads>(w.hist, (uint32_t)a.k, sm, &bstar, &above);
-  const uint32_t total = above + w.hist[bstar];
+  find_threshold_bin<kFinThreads>(hist12, (uint32_t)a.k, sm, &bstar, &above);
+  const uint32_t total = above + hist12[bstar];
   const bool direct = total > cap;
   const float* row = a.scores + (long long)r * a.ld;
   const int W4 = (((n + 31) >> 5) + 3) & ~3;  // words, rounded up to 16 bytes
@@ -329,6 +326,89 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   for (int j = (int)min(written, (uint32_t)a.k) + tid; j < a.k; j += kFinThreads) out[j] = -1;
 }
 
+__global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  const int r = blockIdx.x;
+  const int n = row_valid_count(a, r);
+  int32_t* out = a.idx + (long long)r * a.k;
+  if (n <= a.k) {
+    for (int j = threadIdx.x; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
+    return;
+  }
+  RowWs w = row_ws(a.ws, r, a.k);
+  select_row(a, r, n, out, w.hist, w.ekey, w.eidx, w.meta[0], dyn);
+}
+
+// One block per row does the whole selection (rows up to kRowMaxS scores,
+// k up to kRowMaxK): the 12-bit histogram in LDS over one pass of the row,
+// the threshold bin, the candidates (every score in the bins at or above it)
+// compacted into LDS over a second pass, then select_row.  No workspace, no
+// global atomics, one launch; the row's two passes read scores the indexer
+// has just written (L2 / last-level cache).
+constexpr int kRowMaxS = 32768;    // longer rows: several blocks per row (the multi-launch path) are faster
+constexpr int kRowMaxK = 2048;
+constexpr int kRowCap = 2 * kRowMaxK + 4096;  // cap_for(kRowMaxK)
+constexpr int kRowRegion = 2 * (kRowMaxS / 32) + (1 << kFinDigit) + ((kFinThreads / 64) << kDigitBits) + 64;
+constexpr int kRowUnroll = 8;                 // score loads in flight per thread
+
+__global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t region[kRowRegion];
+  __shared__ __attribute__((aligned(16))) uint32_t hist12[kBins];
+  __shared__ uint32_t ckey[kRowCap], cidx[kRowCap];
+  __shared__ uint32_t ccount;
+  const int r = blockIdx.x;
+  const int n = row_valid_count(a, r);
+  int32_t* out = a.idx + (long long)r * a.k;
+  const int tid = threadIdx.x;
+  if (n <= a.k) {
+    for (int j = tid; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
+    return;
+  }
+  for (int i = tid; i < kBins; i += kFinThreads) hist12[i] = 0u;
+  if (tid == 0) ccount = 0u;
+  __syncthreads();
+  const float* row = a.scores + (long long)r * a.ld;
+  // pass 1: histogram (loads issued kRowUnroll at a time, addresses clamped)
+  for (int e0 = 0; e0 < n; e0 += kFinThreads * kRowUnroll) {
+    uint32_t key[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int e = e0 + u * kFinThreads + tid;
+      key[u] = order_key(row[e < n ? e : n - 1]);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (e0 + u * kFinThreads + tid < n) atomicAdd(&hist12[key[u] >> kBinShift], 1u);
+  }
+  __syncthreads();
+  constexpr int NW = kFinThreads / 64;
+  uint32_t* sm = region + 2 * ((((a.S_max + 31) >> 5) + 3) & ~3) + (1 << kFinDigit) + (NW << kDigitBits);
+  uint32_t bstar, above;
+  find_threshold_bin<kFinThreads>(hist12, (uint32_t)a.k, sm, &bstar, &above);
+  if (above + hist12[bstar] <= (uint32_t)kRowCap) {
+    // pass 2: candidates (exactly above + hist12[bstar] of them)
+    for (int e0 = 0; e0 < n; e0 += kFinThreads * kRowUnroll) {
+      uint32_t key[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + u * kFinThreads + tid;
+        key[u] = order_key(row[e < n ? e : n - 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + u * kFinThreads + tid;
+        if (e < n && (key[u] >> kBinShift) >= bstar) {
+          const uint32_t slot = atomicAdd(&ccount, 1u);
+          ckey[slot] = key[u];
+          cidx[slot] = (uint32_t)e;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  select_row(a, r, n, out, hist12, ckey, cidx, ccount, region);
+}
+
 size_t final_lds_bytes(int S_max, int k) {
   (void)k;
   return (2 * (size_t)((((S_max + 31) >> 5) + 3) & ~3) + ((size_t)1 << kFinDigit) +
@@ -336,6 +416,8 @@ size_t final_lds_bytes(int S_max, int k) {
 }
 
 }  // namespace
+
+bool topk_row_fused(int S_max, int k) { return S_max <= kRowMaxS && k <= kRowMaxK; }
 
 
 // Rows whose valid set fits in k keep every valid position: idx = 0 .. pos,
@@ -374,6 +456,10 @@ void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* str
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
+  if (topk_row_fused(a.S_max, a.k)) {
+    hipLaunchKernelGGL(k_topk_row, dim3((unsigned)a.row_count), dim3(kFinThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);
   if (!a.ws_zeroed) hipLaunchKernelGGL(k_topk_zero, dim3(256), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(k_topk_hist, segs, dim3(kSegThreads), 0, stream, a);

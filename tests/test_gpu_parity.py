@@ -67,11 +67,14 @@ def test_indexer_row_slice_and_ld(dsa_gpu):
     assert np.all(got[:, 3000:] == 7.0), "columns beyond S_max must be untouched"
 
 
-def test_topk_synthetic_ties_and_short_rows(dsa_gpu):
-    _say("[topk] synthetic ties / short rows / concentrated rows")
+@pytest.mark.parametrize("S", [20000, 40000], ids=["one_block_per_row", "several_blocks_per_row"])
+def test_topk_synthetic_ties_and_short_rows(dsa_gpu, S):
+    """Rows up to 32768 scores (k <= 2048) are selected by one block each,
+    longer rows by several; both must follow the rule exactly."""
+    _say(f"[topk] synthetic ties / short rows / concentrated rows, S={S}")
     rng = np.random.default_rng(5)
-    B, q_len, S = 6, 1, 20000
-    seq = np.array([20000, 17, 20000, 20000, 9000, 2049], np.int32)
+    B, q_len = 6, 1
+    seq = np.array([S, 17, S, S, 9000, 2049], np.int32)
     scores = rng.integers(-5, 6, (B, S)).astype(np.float32)          # massive ties
     scores[2] = 1.0                                                    # one value everywhere
     scores[3] = (1.0 + rng.standard_normal(S) * 1e-6).astype(np.float32)  # all in one bin
