@@ -13,6 +13,12 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ReLU as one integer max on the bit pattern: a float with its sign bit set
+// is a negative int32, so max(bits, 0) keeps every x >= +0 and maps every
+// negative x (and -0) to +0.  fmaxf(x, 0.f) would also cost a canonicalising
+// max per value in IEEE mode.  Differs from fmaxf only on NaN input (kept).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256, 2) void k_indexer_fp8(IndexerArgs a) {
         for (int m = 0; m < 4; ++m) {
           const v4f d = mfma_fp8_16x16x128(qf[r][m], kf[blk]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], fmaxf(d[i], 0.f), acc);
+          for (int i = 0; i < 4; ++i) acc = fmaf(wv[r][m][i], relu(d[i]), acc);
         }
         x[r][blk] = acc;
       }

@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
 #pragma unroll
           for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc = fmaf(wv[rr][m][i], fmaxf(d[rr][m][i], 0.f), acc);
+            for (int i = 0; i < 4; ++i) acc = fmaf(wv[rr][m][i], relu(d[rr][m][i]), acc);
           x[rr][blk] = acc;
         }
         __builtin_amdgcn_sched_group_barrier(0x0100, 2, 0);        // the B-operand reads

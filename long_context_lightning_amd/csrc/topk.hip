@@ -345,12 +345,59 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
 // compacted into LDS over a second pass, then select_row.  No workspace, no
 // global atomics, one launch; the row's two passes read scores the indexer
 // has just written (L2 / last-level cache).
-constexpr int kRowMaxS = 32768;    // longer rows: several blocks per row (the multi-launch path) are faster
+// Longest row sent here.  Longer rows go to several blocks per row: at
+// 131072 scores one block takes 47 us against 33 us for the multi-launch
+// path, its LDS histogram atomics (scores crowd into a few bins) being
+// spread over one CU instead of sixteen.
+constexpr int kRowMaxS = 32768;
 constexpr int kRowMaxK = 2048;
 constexpr int kRowCap = 2 * kRowMaxK + 4096;  // cap_for(kRowMaxK)
 constexpr int kRowRegion = 2 * (kRowMaxS / 32) + (1 << kFinDigit) + ((kFinThreads / 64) << kDigitBits) + 64;
 constexpr int kRowUnroll = 8;                 // score loads in flight per thread
 
+// The scores of one pass over a row, kRowUnroll loads per thread in flight:
+// f(key, position) for every valid position, in no particular order.  VEC:
+// 16-byte loads of four scores (row start 16-byte aligned), so a 1024-thread
+// block keeps 128 KB in flight; otherwise 4-byte loads.  Addresses are
+// clamped into the row, so no load sits behind a branch.
+template <bool VEC, typename F>
+__device__ __forceinline__ void row_pass(const float* row, int n, F&& f) {
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    const int last = (n - 1) & ~3;
+    for (int e0 = 0; e0 < n; e0 += 4 * kFinThreads * kRowUnroll) {
+      v4f v[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + 4 * (u * kFinThreads + tid);
+        v[u] = *reinterpret_cast<const v4f*>(row + (e < n ? e : last));
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + 4 * (u * kFinThreads + tid);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (e + c < n) f(order_key(v[u][c]), e + c);
+      }
+    }
+  } else {
+    for (int e0 = 0; e0 < n; e0 += kFinThreads * kRowUnroll) {
+      uint32_t key[kRowUnroll];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + u * kFinThreads + tid;
+        key[u] = order_key(row[e < n ? e : n - 1]);
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        const int e = e0 + u * kFinThreads + tid;
+        if (e < n) f(key[u], e);
+      }
+    }
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t region[kRowRegion];
   __shared__ __attribute__((aligned(16))) uint32_t hist12[kBins];
@@ -368,18 +415,8 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
   if (tid == 0) ccount = 0u;
   __syncthreads();
   const float* row = a.scores + (long long)r * a.ld;
-  // pass 1: histogram (loads issued kRowUnroll at a time, addresses clamped)
-  for (int e0 = 0; e0 < n; e0 += kFinThreads * kRowUnroll) {
-    uint32_t key[kRowUnroll];
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      const int e = e0 + u * kFinThreads + tid;
-      key[u] = order_key(row[e < n ? e : n - 1]);
-    }
-#pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-      if (e0 + u * kFinThreads + tid < n) atomicAdd(&hist12[key[u] >> kBinShift], 1u);
-  }
+  // pass 1: histogram
+  row_pass<VEC>(row, n, [&](uint32_t key, int) { atomicAdd(&hist12[key >> kBinShift], 1u); });
   __syncthreads();
   constexpr int NW = kFinThreads / 64;
   uint32_t* sm = region + 2 * ((((a.S_max + 31) >> 5) + 3) & ~3) + (1 << kFinDigit) + (NW << kDigitBits);
@@ -387,23 +424,13 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
   find_threshold_bin<kFinThreads>(hist12, (uint32_t)a.k, sm, &bstar, &above);
   if (above + hist12[bstar] <= (uint32_t)kRowCap) {
     // pass 2: candidates (exactly above + hist12[bstar] of them)
-    for (int e0 = 0; e0 < n; e0 += kFinThreads * kRowUnroll) {
-      uint32_t key[kRowUnroll];
-#pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
-        const int e = e0 + u * kFinThreads + tid;
-        key[u] = order_key(row[e < n ? e : n - 1]);
+    row_pass<VEC>(row, n, [&](uint32_t key, int e) {
+      if ((key >> kBinShift) >= bstar) {
+        const uint32_t slot = atomicAdd(&ccount, 1u);
+        ckey[slot] = key;
+        cidx[slot] = (uint32_t)e;
       }
-#pragma unroll
-      for (int u = 0; u < kRowUnroll; ++u) {
-        const int e = e0 + u * kFinThreads + tid;
-        if (e < n && (key[u] >> kBinShift) >= bstar) {
-          const uint32_t slot = atomicAdd(&ccount, 1u);
-          ckey[slot] = key[u];
-          cidx[slot] = (uint32_t)e;
-        }
-      }
-    }
+    });
   }
   __syncthreads();
   select_row(a, r, n, out, hist12, ckey, cidx, ccount, region);
@@ -457,7 +484,11 @@ void topk_zero_region(void* ws, int rows, int k, uint32_t** base, long long* str
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
   if (topk_row_fused(a.S_max, a.k)) {
-    hipLaunchKernelGGL(k_topk_row, dim3((unsigned)a.row_count), dim3(kFinThreads), 0, stream, a);
+    const bool vec = (a.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(a.scores) & 15) == 0;
+    if (vec)
+      hipLaunchKernelGGL(k_topk_row<true>, dim3((unsigned)a.row_count), dim3(kFinThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_topk_row<false>, dim3((unsigned)a.row_count), dim3(kFinThreads), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 segs((unsigned)((a.S_max + kSeg - 1) / kSeg), (unsigned)a.row_count);

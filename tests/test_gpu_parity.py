@@ -67,24 +67,35 @@ def test_indexer_row_slice_and_ld(dsa_gpu):
     assert np.all(got[:, 3000:] == 7.0), "columns beyond S_max must be untouched"
 
 
-@pytest.mark.parametrize("S", [20000, 40000], ids=["one_block_per_row", "several_blocks_per_row"])
-def test_topk_synthetic_ties_and_short_rows(dsa_gpu, S):
+TOPK_PATHS = [
+    # name, S, extra columns (ld = S + extra)
+    ("one_block_per_row", 20000, 0),             # 16-byte score loads
+    ("one_block_per_row_odd_ld", 30001, 1),      # ld % 4 != 0: 4-byte loads
+    ("several_blocks_per_row", 40000, 0),        # rows beyond 32768 scores
+]
+
+
+@pytest.mark.parametrize("case", TOPK_PATHS, ids=[c[0] for c in TOPK_PATHS])
+def test_topk_synthetic_ties_and_short_rows(dsa_gpu, case):
     """Rows up to 32768 scores (k <= 2048) are selected by one block each,
-    longer rows by several; both must follow the rule exactly."""
-    _say(f"[topk] synthetic ties / short rows / concentrated rows, S={S}")
+    longer rows (or k > 2048) by several; every path must follow the rule
+    exactly.  Columns past S_max hold a huge score that must never be read."""
+    name, S, extra = case
+    _say(f"[topk] synthetic ties / short rows / concentrated rows, {name}")
     rng = np.random.default_rng(5)
     B, q_len = 6, 1
     seq = np.array([S, 17, S, S, 9000, 2049], np.int32)
-    scores = rng.integers(-5, 6, (B, S)).astype(np.float32)          # massive ties
-    scores[2] = 1.0                                                    # one value everywhere
-    scores[3] = (1.0 + rng.standard_normal(S) * 1e-6).astype(np.float32)  # all in one bin
-    scores[4] = rng.standard_normal(S).astype(np.float32)
+    scores = np.full((B, S + extra), 1e30, np.float32)
+    scores[:, :S] = rng.integers(-5, 6, (B, S))                       # massive ties
+    scores[2, :S] = 1.0                                                # one value everywhere
+    scores[3, :S] = 1.0 + rng.standard_normal(S) * 1e-6                # all in one bin
+    scores[4, :S] = rng.standard_normal(S)
     d_seq = torch.from_numpy(seq).cuda()
     g = dsa_gpu.make_geom(B, q_len, S, d_seq)
     for k in (1, 7, 2048, 4096):
         idx = dsa_gpu.topk(g, torch.from_numpy(scores).cuda(), k).cpu().numpy()
         for r in range(B):
-            want, _ = topk_select(scores[r].astype(np.float64), seq[r] - 1, k)
+            want, _ = topk_select(scores[r, :S].astype(np.float64), seq[r] - 1, k)
             assert np.array_equal(idx[r], want), f"k={k} row {r}"
 
 
