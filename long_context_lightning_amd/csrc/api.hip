@@ -96,6 +96,7 @@ hipError_t run_topk(const TopkArgs& a, hipStream_t stream) {
     c.row_count = (end - r0 < kMaxRowsPerLaunch) ? end - r0 : kMaxRowsPerLaunch;
     c.scores = a.scores + (long long)(r0 - a.row_begin) * a.ld;
     c.idx = a.idx + (long long)(r0 - a.row_begin) * a.k;
+    if (a.rows) c.rows = a.rows + (long long)(r0 - a.row_begin) * a.k;
     c.ws_zeroed = r0 == a.row_begin ? a.ws_zeroed : 0;  // later chunks reuse the workspace
     const hipError_t e = launch_topk(c, stream);
     if (e != hipSuccess) return e;
@@ -234,13 +235,15 @@ dsa_status indexer_scores_impl(const dsa_geom* geom, const dsa_pages* pages, con
 }
 
 // The attention over translated pool rows (paged) or positions (contiguous).
+// rows_ready: the top-k launch has already written the pool rows.
 hipError_t mla_launches(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k, float sm_scale,
                         const void* q, dsa_dtype dtype, const void* kv, const int32_t* idx, void* out, float* lse,
-                        void* mla_ws, int32_t* rows, hipStream_t stream) {
+                        void* mla_ws, int32_t* rows, hipStream_t stream, bool rows_ready = false) {
   MlaArgs a = make_mla_args(geom, H, k, sm_scale, q, kv, idx, out, lse, mla_ws);
   if (pages) {
-    const hipError_t e = launch_page_rows(idx, rows, (int)rows_of(geom), k, geom->q_len, geom->S_max,
-                                          geom->seq_lens, page_map(pages), stream);
+    const hipError_t e = rows_ready ? hipSuccess
+                                    : launch_page_rows(idx, rows, (int)rows_of(geom), k, geom->q_len, geom->S_max,
+                                                       geom->seq_lens, page_map(pages), stream);
     if (e != hipSuccess) return e;
     a.idx = rows;
     a.flat = 1;
@@ -314,7 +317,7 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
     const bool fp8 = index_dtype == DSA_FP8_E4M3FN;
     for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
       const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
-      TopkArgs ta;
+      TopkArgs ta{};
       ta.B = geom->B;
       ta.q_len = geom->q_len;
       ta.S_max = geom->S_max;
@@ -327,6 +330,10 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
       ta.idx = idx_out + (long long)r0 * topk;
       ta.ws = wsb + p.topk_off;
       ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
+      if (pages) {       // the top-k also writes the selection as pool rows
+        ta.rows = reinterpret_cast<int32_t*>(wsb + p.rows_off) + (long long)r0 * topk;
+        ta.pages = page_map(pages);
+      }
       ia.row_begin = r0;
       ia.row_count = rc;
       ia.scores = scores;
@@ -342,7 +349,8 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t to
   }
   if (e != hipSuccess) return DSA_ERR_HIP;
   return hip_status(mla_launches(geom, pages, H, topk, sm_scale, mla_q, mla_dtype, mla_kv, idx_out, out, lse,
-                                 wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream));
+                                 wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream,
+                                 /*rows_ready=*/!p.streaming));
 }
 
 dsa_status cache_append_impl(const dsa_geom* geom, const dsa_pages* pages, const void* k_new, dsa_dtype k_dtype,
@@ -399,7 +407,7 @@ dsa_status dsa_topk(const dsa_geom* geom, const float* scores, int64_t ld, int32
   if (!topk_supported(geom->S_max, k)) return DSA_ERR_UNSUPPORTED;
   const size_t need = dsa_topk_workspace_size(row_count, geom->S_max, k);
   if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
-  TopkArgs a;
+  TopkArgs a{};
   a.B = geom->B;
   a.q_len = geom->q_len;
   a.S_max = geom->S_max;

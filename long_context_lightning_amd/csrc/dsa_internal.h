@@ -53,6 +53,12 @@ struct PageMap {
   }
 };
 
+// Pool row of position s for a query of sequence b at position pos; -1 when
+// the query may not select s (negative, or past pos).
+__device__ __forceinline__ int32_t page_row(int32_t s, int pos, int b, const PageMap& pm) {
+  return (s >= 0 && s <= pos) ? pm.row(b, s) : -1;
+}
+
 // Length of sequence b clamped into [0, S_max].
 __device__ __forceinline__ int clamped_len(const int32_t* seq_lens, int b, int S_max) {
   int L = seq_lens[b];
@@ -223,6 +229,8 @@ struct TopkArgs {
   int32_t* idx;           // [row_count, k]
   void* ws;
   int ws_zeroed;          // the counters in ws are already zero (cleared by the indexer launch)
+  int32_t* rows;          // optional [row_count, k]: the selection as pool rows of `pages` (-1 where idx is)
+  PageMap pages;
 };
 
 // Per-block fp8 quantisation (launch_quantize: rows -> codes/scales;

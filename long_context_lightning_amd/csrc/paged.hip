@@ -19,10 +19,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int32_t page_row(int32_t s, int pos, int b, const PageMap& pm) {
-  return (s >= 0 && s <= pos) ? pm.row(b, s) : -1;
-}
-
 __global__ __launch_bounds__(kThreads) void k_page_rows4(const int32_t* idx, int32_t* rows, long long nq, int k,
                                                          int q_len, int S_max, const int32_t* seq_lens,
                                                          PageMap pm) {

@@ -326,6 +326,19 @@ __device__ void select_row(const TopkArgs& a, int r, int n, int32_t* out, const 
   for (int j = (int)min(written, (uint32_t)a.k) + tid; j < a.k; j += kFinThreads) out[j] = -1;
 }
 
+// With a.rows set, the row's selection (already in `out`, written by this
+// block before the barrier) is also written as pool rows of a.pages, so a
+// paged attention needs no translation launch of its own.
+__device__ __forceinline__ void emit_pool_rows(const TopkArgs& a, int r, const int32_t* out) {
+  if (!a.rows) return;
+  __syncthreads();
+  const int t = a.row_begin + r;
+  const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);
+  const int b = t / a.q_len;
+  int32_t* rows = a.rows + (long long)r * a.k;
+  for (int j = threadIdx.x; j < a.k; j += blockDim.x) rows[j] = page_row(out[j], pos, b, a.pages);
+}
+
 __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   const int r = blockIdx.x;
@@ -333,10 +346,11 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
   int32_t* out = a.idx + (long long)r * a.k;
   if (n <= a.k) {
     for (int j = threadIdx.x; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
-    return;
+  } else {
+    RowWs w = row_ws(a.ws, r, a.k);
+    select_row(a, r, n, out, w.hist, w.ekey, w.eidx, w.meta[0], dyn);
   }
-  RowWs w = row_ws(a.ws, r, a.k);
-  select_row(a, r, n, out, w.hist, w.ekey, w.eidx, w.meta[0], dyn);
+  emit_pool_rows(a, r, out);
 }
 
 // One block per row does the whole selection (rows up to kRowMaxS scores,
@@ -409,6 +423,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
   const int tid = threadIdx.x;
   if (n <= a.k) {
     for (int j = tid; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
+    emit_pool_rows(a, r, out);
     return;
   }
   for (int i = tid; i < kBins; i += kFinThreads) hist12[i] = 0u;
@@ -434,6 +449,7 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_row(TopkArgs a) {
   }
   __syncthreads();
   select_row(a, r, n, out, hist12, ckey, cidx, ccount, region);
+  emit_pool_rows(a, r, out);
 }
 
 size_t final_lds_bytes(int S_max, int k) {

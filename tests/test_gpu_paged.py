@@ -87,6 +87,7 @@ PAGED = [
     ("p128_long_q", 1, 300, [700], 700, 128, 16, 128, True, "normal", 0),
     ("p64_f32", 2, 20, [512, 100], 512, 64, 16, 64, False, "normal", 1),
     ("p64_keep_all", 2, 40, [300, 41], 300, 512, 16, 64, True, "normal", 0),   # S_max <= topk: indexer bypassed
+    ("p64_long_and_short", 2, 1, [40000, 100], 40000, 256, 16, 64, True, "normal", 0),  # multi-launch top-k
 ]
 
 
