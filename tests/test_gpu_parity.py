@@ -108,6 +108,26 @@ MLA_CASES = [
 ]
 
 
+def test_topk_largest_rows(dsa_gpu):
+    """The largest rows the top-k accepts (S_max = 262144) at k = 2048 and
+    the largest k (4096): ragged lengths, a tied row, a row of exactly k + 1
+    valid positions; exact against the oracle's rule."""
+    _say("[topk] S_max = 262144, k in (2048, 4096)")
+    rng = np.random.default_rng(8)
+    S = 262144
+    seq = np.array([S, 100003, 4097, S], np.int32)
+    B = len(seq)
+    scores = rng.standard_normal((B, S)).astype(np.float32)
+    scores[3] = rng.integers(-3, 4, S)                          # heavy ties over the whole row
+    d_seq = torch.from_numpy(seq).cuda()
+    g = dsa_gpu.make_geom(B, 1, S, d_seq)
+    for k in (2048, 4096):
+        idx = dsa_gpu.topk(g, torch.from_numpy(scores).cuda(), k).cpu().numpy()
+        for r in range(B):
+            want, _ = topk_select(scores[r].astype(np.float64), seq[r] - 1, k)
+            assert np.array_equal(idx[r], want), f"k={k} row {r}"
+
+
 @pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
 def test_sparse_mla(dsa_gpu, case):
     name, B, q_len, seq, S, k, H, bf16 = case
