@@ -74,6 +74,20 @@ def test_topk_validation_and_workspace():
     assert lib.dsa_topk(ctypes.byref(big), P(FAKE), 1 << 20, 0, 1, 256, P(FAKE), P(FAKE), 1 << 30, None) == 2
 
 
+def test_topk_empty_calls_and_the_largest_rows():
+    """No rows: success with nothing launched (before any size check); an
+    empty geometry is invalid; rows of 262145 scores are unsupported (262144,
+    the largest accepted, runs in the GPU parity tests)."""
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=1, S=5000)
+    assert lib.dsa_topk(ctypes.byref(g), P(FAKE), 5000, 2, 0, 256, P(FAKE), P(FAKE), 0, None) == 0
+    empty = _geom(B=0, q_len=1, S=5000)
+    assert lib.dsa_topk(ctypes.byref(empty), P(FAKE), 5000, 0, 0, 256, P(FAKE), P(FAKE), 1 << 30, None) == 1
+    lim = _geom(B=1, q_len=1, S=262145)
+    assert lib.dsa_topk(ctypes.byref(lim), P(FAKE), 262145, 0, 1, 4096, P(FAKE), P(FAKE), 1 << 30, None) == 2
+
+
 def test_sparse_mla_validation():
     lib = lcl.load()
     g = _geom(B=1, q_len=2, S=100)
