@@ -29,7 +29,7 @@ namespace {
 constexpr int kBins = 4096;     // histogram bins: top 12 bits of the order key (sign, exponent, 3 mantissa bits)
 constexpr int kBinShift = 20;
 constexpr int kSeg = 8192;      // scores per hist/gather block
-constexpr int kSegThreads = 256;
+constexpr int kSegThreads = 512;
 constexpr int kFinThreads = 1024;
 constexpr int kDigitBits = 8;   // radix digit width of the selection from a score row
 constexpr int kFinDigit = 10;   // radix digit width of the selection inside bin b*
