@@ -29,8 +29,9 @@
 // row g of a score block holds keys 4g..4g+3 and 16+4g..16+4g+3, which is
 // the k-slice 8g..8g+7 of the value product.
 // With one split the block writes the bf16 output and the log-sum-exp; with
-// several each split writes its bf16 output normalised by its own sum plus
-// (max, sum), and a combine kernel merges them.
+// several each split writes its fp32 output normalised by its own sum plus
+// (max, sum), and a combine kernel merges them (the output is rounded to
+// bf16 once, after the merge).
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -106,7 +107,7 @@ __host__ __device__ inline int mla_per_split(int k, int ns) {
 }
 
 struct Partials {
-  uint16_t* o;  // [T][ns][H][512] bf16, normalised by the split's own sum
+  float* o;     // [T][ns][H][512] fp32, normalised by the split's own sum
   float* ml;    // [T][ns][H][2]   (max in log2 units, sum)
 };
 
@@ -114,7 +115,7 @@ __device__ __forceinline__ Partials partials(const MlaArgs& a, int ns) {
   Partials p;
   const size_t T = (size_t)a.row_count;
   p.ml = static_cast<float*>(a.ws);
-  p.o = reinterpret_cast<uint16_t*>(p.ml + T * ns * a.H * 2);
+  p.o = p.ml + T * ns * a.H * 2;
   return p;
 }
 
@@ -527,6 +528,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
     }
   }
   __syncthreads();
+  if (ns > 1) {
+    // fp32 split partial straight from the accumulators: lane (c, g) holds
+    // dims 128w + 16db + 4g .. +3 of head 16hb + c, one 16-byte store each
+    // (each head's 16-dim piece is 64 contiguous bytes).
+#pragma unroll
+    for (int hb = 0; hb < kMaxHB; ++hb) {
+      if (!(hb < NHB)) break;
+      const int head = 16 * hb + c;
+      const float inv = hinv[head];
+      float* prow = P.o + (((size_t)r * ns + split) * a.H + head) * kDV + (kDV / kWaves) * wave + 4 * g;
+#pragma unroll
+      for (int db = 0; db < kDbW; ++db)
+        *reinterpret_cast<v4f*>(prow + 16 * db) = acc_o[db][hb] * inv;
+    }
+    return;
+  }
   // Output through LDS (the ring is free now): each wave stages four 16-head
   // blocks at a time as rows of its 128 dims, then stores whole 256-byte
   // pieces of the output rows.
@@ -556,18 +573,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       const int hh = 64 * half + hr;
       if (hh < 16 * NHB) {
         const v4i v = *reinterpret_cast<const v4i*>(stage + hr * kStageRS + 16 * (lane & 15));
-        uint16_t* orow = ns == 1 ? static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hh) * kDV
-                                 : P.o + (((size_t)r * ns + split) * a.H + hh) * kDV;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hh) * kDV;
         *reinterpret_cast<v4i*>(orow + (kDV / kWaves) * wave + 8 * (lane & 15)) = v;
       }
     }
   }
 }
 
-// Merge split partials: each split stored its output normalised by its own
-// sum l_s together with (m_s, l_s); out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s.
+// Merge split partials: each split stored its fp32 output normalised by its
+// own sum l_s together with (m_s, l_s);
+// out = sum_s 2^(m_s-M) l_s o_s / sum_s 2^(m_s-M) l_s, rounded to bf16 once.
 // A wave merges one (row, head): lane l holds dims 8l..8l+7, so each split's
-// partial row is one contiguous 1 KB load (all issued before any is used).
+// partial row is one contiguous 2 KB load (all issued before any is used).
 // Blocks for a row run on the XCD that ran its first split (the split
 // kernel gives XCD x the flat (row, split) indices [x*per_xcd,
 // (x+1)*per_xcd)), whose L2 saw the partials written.
@@ -586,14 +603,15 @@ __global__ __launch_bounds__(64 * kCombineHeads) void k_mla_combine(MlaArgs a, i
   const int t = a.row_begin + r;
   const Partials P = partials(a, ns);
   float ms[kCombineMaxSplits], ls[kCombineMaxSplits];
-  v4i o[kCombineMaxSplits];
+  v4f o[kCombineMaxSplits][2];
 #pragma unroll
   for (int sp = 0; sp < kCombineMaxSplits; ++sp) {
     if (sp < ns) {
       const size_t rs = ((size_t)r * ns + sp) * a.H + h;
       ms[sp] = P.ml[rs * 2];
       ls[sp] = P.ml[rs * 2 + 1];
-      o[sp] = *reinterpret_cast<const v4i*>(P.o + rs * kDV + 8 * lane);
+      o[sp][0] = *reinterpret_cast<const v4f*>(P.o + rs * kDV + 8 * lane);
+      o[sp][1] = *reinterpret_cast<const v4f*>(P.o + rs * kDV + 8 * lane + 4);
     }
   }
   float M = -INFINITY;
@@ -610,11 +628,7 @@ __global__ __launch_bounds__(64 * kCombineHeads) void k_mla_combine(MlaArgs a, i
       const float wgt = exp2f(ms[sp] - M) * ls[sp];
       wsum += wgt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = (uint32_t)o[sp][e];
-        acc[2 * e] += wgt * __uint_as_float(u << 16);
-        acc[2 * e + 1] += wgt * __uint_as_float(u & 0xFFFF0000u);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * o[sp][e >> 2][e & 3];
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -690,7 +704,7 @@ size_t mla_workspace_bytes(int T, int H, int k, int is_bf16) {
   if (!is_bf16 || T <= 0) return 0;
   const int ns = mla_splits(T, k);
   if (ns == 1) return 0;
-  return (size_t)T * ns * H * (2 * sizeof(float) + kDV * sizeof(uint16_t));
+  return (size_t)T * ns * H * (2 * sizeof(float) + kDV * sizeof(float));
 }
 
 bool mla_f32_supported(int k) { return k <= kF32MaxK; }
