@@ -158,7 +158,8 @@ DSA_API size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H
 
 /* The whole forward path: indexer -> top-k -> sparse MLA, on one stream.
  * Arguments as in the three calls above (index_* = the indexer inputs,
- * mla_* = the attention inputs, both at the same geometry).  idx_out
+ * mla_* = the attention inputs, both at the same geometry; H and topk in
+ * the order of dsa_sparse_mla's H and k).  idx_out
  * [T, topk] int32 receives the selection (ascending, -1 padded); it may be
  * NULL, and the selection then lives in the workspace, which must hold
  * T * topk * 4 bytes (rounded up to 256) beyond the size query's value.
@@ -171,7 +172,7 @@ DSA_API size_t dsa_sparse_mla_workspace_size(int32_t B, int32_t q_len, int32_t H
  * bypassed) and neither the indexer nor the top-k runs; the index inputs are
  * still validated.
  * ws >= dsa_forward_workspace_size(...) bytes. */
-DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale,
+DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t H, int32_t topk, float sm_scale,
                        const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
                        const void* index_w, dsa_dtype index_w_dtype,
                        const void* index_k, const float* index_k_scale,
@@ -271,7 +272,7 @@ DSA_API size_t dsa_sparse_mla_paged_workspace_size(int32_t B, int32_t q_len, int
  * dsa_indexer_scores_paged, mla_kv_pool as in dsa_sparse_mla_paged).
  * Every shape scores into the workspace (no streamed prefill).
  * ws >= dsa_forward_paged_workspace_size(...) bytes. */
-DSA_API dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H,
+DSA_API dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t topk,
                        float sm_scale,
                        const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
                        const void* index_w, dsa_dtype index_w_dtype,
@@ -341,6 +342,28 @@ DSA_API dsa_status dsa_indexer_kl(const dsa_geom* geom, int32_t H, float sm_scal
                           const float* scores, int64_t ld, const int32_t* idx, int32_t k,
                           float* kl, float* loss, void* ws, size_t ws_bytes, hipStream_t stream);
 DSA_API size_t dsa_indexer_kl_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t k);
+
+/* One workspace query for every call that takes a workspace.  Returns a
+ * byte count that suffices for the named call at this geometry with ANY
+ * dtype combination the call supports (the maximum of its own
+ * *_workspace_size query over them), so a caller can size one buffer before
+ * it knows the dtypes.  k is the top-k / selection width (dsa_topk's k,
+ * dsa_sparse_mla's k, dsa_forward's topk, dsa_indexer_kl's k with 0 = every
+ * visible position); H the MLA heads.  For DSA_CALL_TOPK the rows are all
+ * B*q_len rows.  The forward sizes assume idx_out != NULL (with NULL add
+ * B*q_len*k*4 bytes rounded up to 256).  Returns 0 for calls that need no
+ * workspace, for non-positive sizes and for an unknown which_call. */
+typedef enum {
+  DSA_CALL_TOPK = 0,
+  DSA_CALL_SPARSE_MLA = 1,
+  DSA_CALL_FORWARD = 2,
+  DSA_CALL_SPARSE_MLA_PAGED = 3,
+  DSA_CALL_FORWARD_PAGED = 4,
+  DSA_CALL_MHA_PREFILL = 5,
+  DSA_CALL_INDEXER_KL = 6
+} dsa_call;
+DSA_API size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t k,
+                                  int which_call);
 
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);

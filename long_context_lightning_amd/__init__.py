@@ -72,6 +72,7 @@ def load(path=None):
         "dsa_mha_prefill_workspace_size": (sz, [i32, i32, i32]),
         "dsa_indexer_kl": (i32, [gp, i32, f32, vp, vp, i32, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]),
         "dsa_indexer_kl_workspace_size": (sz, [i32, i32, i32, i32]),
+        "dsa_workspace_size": (sz, [i32, i32, i32, i32, i32, ctypes.c_int]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -89,7 +90,11 @@ ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "d
                  "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
                  "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_mha_prefill",
                  "dsa_mha_prefill_workspace_size", "dsa_indexer_kl", "dsa_indexer_kl_workspace_size",
-                 "dsa_status_string", "dsa_version")
+                 "dsa_workspace_size", "dsa_status_string", "dsa_version")
+
+# which_call values of dsa_workspace_size
+CALL_TOPK, CALL_SPARSE_MLA, CALL_FORWARD, CALL_SPARSE_MLA_PAGED, CALL_FORWARD_PAGED, CALL_MHA_PREFILL, \
+    CALL_INDEXER_KL = range(7)
 
 
 def _ptr(t):
@@ -196,6 +201,12 @@ def indexer_scores(geom, q, w, k, k_scale=None, q_scale=None, row_begin=0, row_c
     return scores
 
 
+def workspace_size(B, q_len, S_max, H, k, which_call):
+    """dsa_workspace_size: bytes enough for ``which_call`` (a CALL_* value) at
+    this geometry with any supported dtype combination."""
+    return int(load().dsa_workspace_size(B, q_len, S_max, H, k, which_call))
+
+
 def topk_workspace_size(row_count, S_max, k):
     return int(load().dsa_topk_workspace_size(row_count, S_max, k))
 
@@ -299,7 +310,7 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
     _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == _cache_shape(geom, pages, (128,)),
           "indexer shapes mismatch")
     _need(tuple(mla_kv.shape) == _cache_shape(geom, pages, (576,)) and mla_q.shape[0] == T, "MLA shapes mismatch")
-    args = (topk_k, H, float(sm_scale), _ptr(index_q), idt, _ptr(index_q_scale), _ptr(index_w), _w_dtype(index_w),
+    args = (H, topk_k, float(sm_scale), _ptr(index_q), idt, _ptr(index_q_scale), _ptr(index_w), _w_dtype(index_w),
             _ptr(index_k), _ptr(index_k_scale), _ptr(mla_q), _ptr(mla_kv), mdt, _ptr(idx), _ptr(out), _ptr(lse),
             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     if pages is None:

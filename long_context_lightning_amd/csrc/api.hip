@@ -265,7 +265,7 @@ dsa_status sparse_mla_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t
   return hip_status(mla_launches(geom, pages, H, k, sm_scale, q, dtype, kv, idx, out, lse, ws, rows, stream));
 }
 
-dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H, float sm_scale,
+dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t topk, float sm_scale,
                         const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
                         const void* index_w, dsa_dtype index_w_dtype, const void* index_k,
                         const float* index_k_scale, const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype,
@@ -458,23 +458,23 @@ size_t dsa_forward_paged_workspace_size(int32_t B, int32_t q_len, int32_t S_max,
   return plan_forward(B, q_len, S_max, H, topk, index_dtype, mla_dtype, true).total;
 }
 
-dsa_status dsa_forward(const dsa_geom* geom, int32_t topk, int32_t H, float sm_scale, const void* index_q,
+dsa_status dsa_forward(const dsa_geom* geom, int32_t H, int32_t topk, float sm_scale, const void* index_q,
                        dsa_dtype index_dtype, const float* index_q_scale, const void* index_w,
                        dsa_dtype index_w_dtype, const void* index_k, const float* index_k_scale,
                        const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype, int32_t* idx_out, void* out,
                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return forward_impl(geom, nullptr, topk, H, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+  return forward_impl(geom, nullptr, H, topk, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
                       index_k, index_k_scale, mla_q, mla_kv, mla_dtype, idx_out, out, lse, ws, ws_bytes, stream);
 }
 
-dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, int32_t H, float sm_scale,
+dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t topk, float sm_scale,
                              const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
                              const void* index_w, dsa_dtype index_w_dtype, const void* index_k_pool,
                              const float* index_k_scale_pool, const void* mla_q, const void* mla_kv_pool,
                              dsa_dtype mla_dtype, int32_t* idx_out, void* out, float* lse, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
   if (!pages) return DSA_ERR_INVALID_ARG;
-  return forward_impl(geom, pages, topk, H, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+  return forward_impl(geom, pages, H, topk, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
                       index_k_pool, index_k_scale_pool, mla_q, mla_kv_pool, mla_dtype, idx_out, out, lse, ws,
                       ws_bytes, stream);
 }
@@ -577,6 +577,44 @@ dsa_status dsa_indexer_kl(const dsa_geom* geom, int32_t H, float sm_scale, const
   a.row_begin = 0;
   a.row_count = (int)rows_of(geom);
   return hip_status(launch_indexer_kl(a, stream));
+}
+
+size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t k, int which_call) {
+  if (B < 1 || q_len < 1 || S_max < 1 || H < 1 || k < 0) return 0;
+  if ((long long)B * q_len > 0x7FFFFFFFLL) return 0;
+  const dsa_dtype mla_dts[2] = {DSA_BF16, DSA_F32};
+  const dsa_dtype idx_dts[2] = {DSA_FP8_E4M3FN, DSA_F32};
+  size_t best = 0;
+  auto keep = [&](size_t v) { best = v > best ? v : best; };
+  switch (which_call) {
+    case DSA_CALL_TOPK:
+      if (k >= 1) keep(dsa_topk_workspace_size(B * q_len, S_max, k));
+      break;
+    case DSA_CALL_SPARSE_MLA:
+    case DSA_CALL_SPARSE_MLA_PAGED:
+      if (k >= 1)
+        for (dsa_dtype m : mla_dts)
+          keep(which_call == DSA_CALL_SPARSE_MLA ? dsa_sparse_mla_workspace_size(B, q_len, H, k, m)
+                                                 : dsa_sparse_mla_paged_workspace_size(B, q_len, H, k, m));
+      break;
+    case DSA_CALL_FORWARD:
+    case DSA_CALL_FORWARD_PAGED:
+      if (k >= 1)
+        for (dsa_dtype i : idx_dts)
+          for (dsa_dtype m : mla_dts)
+            keep(which_call == DSA_CALL_FORWARD ? dsa_forward_workspace_size(B, q_len, S_max, H, k, i, m)
+                                                : dsa_forward_paged_workspace_size(B, q_len, S_max, H, k, i, m));
+      break;
+    case DSA_CALL_MHA_PREFILL:
+      keep(dsa_mha_prefill_workspace_size(B, S_max, H));
+      break;
+    case DSA_CALL_INDEXER_KL:
+      keep(dsa_indexer_kl_workspace_size(B, q_len, S_max, k));
+      break;
+    default:
+      break;
+  }
+  return best;
 }
 
 const char* dsa_status_string(dsa_status s) {

@@ -169,7 +169,7 @@ def test_paged_validation():
 
     fneed = lib.dsa_forward_paged_workspace_size(2, 1, 256, 128, 2048, 2, 1)
     assert fneed > lib.dsa_forward_workspace_size(2, 1, 256, 128, 2048, 2, 1)
-    fwd = lambda pg, wsb: lib.dsa_forward_paged(ctypes.byref(g), pg, 2048, 128, 0.1, P(FAKE), 2, None, P(FAKE), 1,
+    fwd = lambda pg, wsb: lib.dsa_forward_paged(ctypes.byref(g), pg, 128, 2048, 0.1, P(FAKE), 2, None, P(FAKE), 1,
                                                 P(FAKE), None, P(FAKE), P(FAKE), 1, P(FAKE), P(FAKE), None, P(FAKE),
                                                 wsb, None)
     assert fwd(None, fneed) == 1
@@ -223,7 +223,44 @@ def test_forward_without_idx_out_needs_the_selection_in_the_workspace():
     P = ctypes.c_void_p
     g = _geom(B=2, q_len=1, S=4096)
     need = lib.dsa_forward_workspace_size(2, 1, 4096, 128, 512, 2, 1)
-    call = lambda wsb: lib.dsa_forward(ctypes.byref(g), 512, 128, 0.1, P(FAKE), 2, None, P(FAKE), 1, P(FAKE), None,
+    call = lambda wsb: lib.dsa_forward(ctypes.byref(g), 128, 512, 0.1, P(FAKE), 2, None, P(FAKE), 1, P(FAKE), None,
                                        P(FAKE), P(FAKE), 1, None, P(FAKE), None, P(FAKE), wsb, None)
     assert call(need) == 3                          # the 2 x 512 selection does not fit
     assert call(need + 2 * 512 * 4 - 1) == 3
+
+
+def test_forward_takes_heads_before_topk():
+    """dsa_forward(geom, H, topk, ...), the order of dsa_sparse_mla(geom, H, k, ...):
+    H = 100 is no multiple of 16 (bf16 attention: DSA_ERR_UNSUPPORTED), while
+    the swapped reading would see H = 512 > 128 (DSA_ERR_INVALID_ARG)."""
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    g = _geom(B=2, q_len=1, S=4096)
+    for fn, extra in ((lib.dsa_forward, ()), (lib.dsa_forward_paged, (ctypes.byref(_pages(max_pages=64)),))):
+        st = fn(ctypes.byref(g), *extra, 100, 512, 0.1, P(FAKE), 2, None, P(FAKE), 1, P(FAKE), None, P(FAKE),
+                P(FAKE), 1, P(FAKE), P(FAKE), None, P(FAKE), 1 << 40, None)
+        assert st == 2, st
+    assert lib.dsa_sparse_mla(ctypes.byref(g), 100, 512, 0.1, P(FAKE), 1, P(FAKE), P(FAKE), P(FAKE), None, P(FAKE),
+                              1 << 40, None) == 2
+
+
+def test_single_workspace_query_covers_every_dtype():
+    lib = lcl.load()
+    B, q_len, S, H, k = 16, 2, 131072, 128, 2048
+    ws = lambda call, kk=k: lib.dsa_workspace_size(B, q_len, S, H, kk, call)
+    assert ws(lcl.CALL_TOPK) == lib.dsa_topk_workspace_size(B * q_len, S, k)
+    assert ws(lcl.CALL_SPARSE_MLA) == max(lib.dsa_sparse_mla_workspace_size(B, q_len, H, k, dt) for dt in (0, 1))
+    assert ws(lcl.CALL_FORWARD) == max(lib.dsa_forward_workspace_size(B, q_len, S, H, k, i, m)
+                                       for i in (0, 2) for m in (0, 1))
+    assert ws(lcl.CALL_FORWARD_PAGED) == max(lib.dsa_forward_paged_workspace_size(B, q_len, S, H, k, i, m)
+                                             for i in (0, 2) for m in (0, 1))
+    assert ws(lcl.CALL_SPARSE_MLA_PAGED) == max(lib.dsa_sparse_mla_paged_workspace_size(B, q_len, H, k, dt)
+                                                for dt in (0, 1))
+    assert ws(lcl.CALL_MHA_PREFILL) == lib.dsa_mha_prefill_workspace_size(B, S, H)
+    assert ws(lcl.CALL_INDEXER_KL) == lib.dsa_indexer_kl_workspace_size(B, q_len, S, k)
+    assert ws(lcl.CALL_INDEXER_KL, 0) == lib.dsa_indexer_kl_workspace_size(B, q_len, S, 0)
+    # a long prefill: the fp8 streamed plan and the f32 score-chunk plan differ; the maximum is returned
+    pre = lib.dsa_workspace_size(1, 65536, 65536, 128, 2048, lcl.CALL_FORWARD)
+    assert pre == max(lib.dsa_forward_workspace_size(1, 65536, 65536, 128, 2048, i, m) for i in (0, 2) for m in (0, 1))
+    assert lib.dsa_workspace_size(B, q_len, S, H, k, 99) == 0
+    assert lib.dsa_workspace_size(0, q_len, S, H, k, lcl.CALL_FORWARD) == 0
