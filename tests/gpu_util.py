@@ -4,7 +4,7 @@ against the oracle with the stated tolerances."""
 import numpy as np
 import torch
 
-from oracle import indexer_scores, query_positions, sparse_mla, topk_select
+from oracle import decode_bf16, indexer_scores, query_positions, sparse_mla, topk_select
 
 # Tolerances of the DSA forward path (float64 oracle vs the HIP path):
 SCORE_RTOL = 2e-2      # indexer scores, relative (fp8 inputs, fp32 accumulate)
@@ -112,31 +112,70 @@ def bf16_ulp(x):
 
 
 def attention_tolerance(ref, bf16_output):
-    """1e-2 absolute.  For a bf16 output, where the format's own spacing at the
-    exact value exceeds 1e-2 (|x| >= 2) the bound is one bf16 ulp: no bf16
-    number need lie within 1e-2 of such a value."""
+    """1e-2 absolute.  For a bf16 output the bound is raised to half a bf16
+    ulp of the exact value where that is larger (|x| >= 4): the nearest bf16
+    number to x is within half an ulp, and no closer one need exist."""
     if not bf16_output:
         return ATTN_ATOL
-    return np.maximum(ATTN_ATOL, bf16_ulp(ref))
+    return np.maximum(ATTN_ATOL, 0.5 * bf16_ulp(ref))
+
+
+U_BF16 = 2.0 ** -9   # unit roundoff of bfloat16 (round to nearest, ties to even)
+
+
+def weight_rounding_bound(qm, qm_fmt, kv, kv_fmt, b, sel, t, h, sm_scale):
+    """Per value dim: the most the bf16 rounding of the attention weights can
+    move an exact output, u/(1-u) * sum_m p_m |v_m - o|.  The pages' MLA
+    forward casts the fp32 softmax to the value dtype before the value
+    product ("详解DSA", MLA code block: scores.type_as(x)); with the weights
+    p_m (1 + d_m), |d_m| <= u, and the normaliser summing the same rounded
+    weights, the output moves by sum_m p_m d_m (v_m - o) / sum_m p_m (1 + d_m).
+    A 10% margin covers the fp32 score and accumulation error."""
+    c = decode_bf16(kv[b, sel]) if kv_fmt == "bf16" else np.asarray(kv[b, sel], np.float64)
+    q = decode_bf16(qm[t, h]) if qm_fmt == "bf16" else np.asarray(qm[t, h], np.float64)
+    z = sm_scale * (c @ q)
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    v = c[:, :512]
+    o = p @ v
+    return 1.1 * U_BF16 / (1 - U_BF16) * (p @ np.abs(v - o)) + 1e-6 * np.abs(v).max()
 
 
 def check_attention(out_gpu, lse_gpu, up, idx, rows):
     """Attention verdict on the GPU's own index sets: |out - oracle| within
-    attention_tolerance elementwise; lse within 1e-2."""
+    attention_tolerance elementwise; a bf16 element beyond it may exceed half
+    an ulp only by the weight-rounding bound of its (row, head), the case of
+    an exact value within that bound of a bf16 rounding midpoint.  lse within
+    1e-2."""
     wl = up.wl
     idx_full = np.full((wl.T, idx.shape[1]), -1, dtype=np.int64)
     idx_full[rows] = idx
     ref, ref_lse = sparse_mla(up.qm, wl.qm_fmt, up.kv, wl.kv_fmt, idx_full, wl.seq_lens, wl.q_len, wl.sm_scale,
                               rows=rows)
     err = np.abs(out_gpu - ref)
-    tol = attention_tolerance(ref, wl.qm_fmt == "bf16")
+    bf16 = wl.qm_fmt == "bf16"
+    tol = attention_tolerance(ref, bf16)
     bad = err > tol
+    n_allow = 0
+    if bf16 and bad.any():
+        batch, _ = query_positions(wl.seq_lens, wl.q_len)
+        for r, h in sorted(set(zip(*np.nonzero(bad.any(axis=2))))):
+            t = int(np.asarray(rows)[r])
+            sel = idx_full[t][idx_full[t] >= 0]
+            eps = weight_rounding_bound(up.qm, wl.qm_fmt, up.kv, wl.kv_fmt, int(batch[t]), sel, t, h, wl.sm_scale)
+            allow = 0.5 * bf16_ulp(ref[r, h]) + eps
+            n_allow += int((bad[r, h] & (err[r, h] <= allow)).sum())
+            bad[r, h] &= err[r, h] > allow
     assert not bad.any(), (f"attention error {err[bad].max():.3g} above tolerance at {int(bad.sum())} elements "
                            f"(max abs error {err.max():.3g})")
-    err = float(err.max())
+    err_max = float(err.max())
+    small = np.abs(ref) < 2.0
+    err_small = float(err[small].max()) if small.any() else 0.0
+    print(f"  attention: max |out - oracle| = {err_max:.3g} (max |ref| = {np.abs(ref).max():.3g}; "
+          f"{err_small:.3g} where |ref| < 2; {n_allow} elements within the weight-rounding allowance)", flush=True)
     if lse_gpu is not None:
         fin = np.isfinite(ref_lse)
         assert np.array_equal(np.isfinite(lse_gpu), fin)
         lerr = np.abs(lse_gpu[fin] - ref_lse[fin]).max() if fin.any() else 0.0
         assert lerr <= 1e-2, f"lse error {lerr:.3g}"
-    return float(err)
+    return err_max

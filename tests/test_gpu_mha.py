@@ -4,8 +4,8 @@ against the float64 oracle ``oracle.mha_prefill``.
 The decompressed keys and values are bf16 tensors, as the output of the bf16
 ``wkv_b`` Linear is in the pages' MLA forward code block; the oracle rounds
 them the same way (``round_bf16=True``) and is exact from there on.
-Tolerance: the attention bar of the MQA path (1e-2 absolute, or one bf16 ulp
-of the exact value where that is larger); lse within 1e-2.
+Tolerance: the attention bar of the MQA path (1e-2 absolute, or half a bf16
+ulp of the exact value where that is larger); lse within 1e-2.
 """
 
 import numpy as np
