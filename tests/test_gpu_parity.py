@@ -214,6 +214,26 @@ def test_full_decode(dsa_gpu, name):
     check_attention(from_dev(out), lse.cpu().numpy(), up, gi.astype(np.int64), np.arange(wl.T))
 
 
+def _check_sampled_scores(lcl, up, g, sample):
+    """dsa_indexer_scores on the sampled rows (row slices of the ABI, one
+    launch per run of consecutive rows) against the oracle: the X12 criterion
+    on the very scores the streamed forward never writes out."""
+    wl = up.wl
+    runs = np.split(sample, np.nonzero(np.diff(sample) != 1)[0] + 1)
+    got = np.empty((len(sample), wl.S_max), np.float32)
+    r = 0
+    for run in runs:
+        sc = lcl.indexer_scores(g, up.d_qi, up.d_w, up.d_ki, k_scale=up.d_ks, row_begin=int(run[0]),
+                                row_count=len(run))
+        torch.cuda.synchronize()
+        got[r:r + len(run)] = sc.cpu().numpy()
+        r += len(run)
+    ref = up.oracle_scores(rows=sample)
+    worst = check_scores(got, ref, wl.positions()[sample])
+    _say(f"  indexer scores on {len(sample)} sampled rows: worst relative error {worst:.3g}")
+    return ref
+
+
 def test_full_prefill8k_planted(dsa_gpu):
     _say("[full] prefill8k planted (streaming path)")
     wl = standard_workload("prefill8k")
@@ -228,25 +248,27 @@ def test_full_prefill8k_planted(dsa_gpu):
     gi = idx.cpu().numpy()
     for t in wl.planted_rows:
         assert np.array_equal(gi[t], wl.planted_set), f"planted row {t} lost its planted set"
-    ref = up.oracle_scores(rows=sample)
+    ref = _check_sampled_scores(dsa_gpu, up, g, sample)
     check_topk(gi[sample], ref, wl.positions()[sample], wl.topk)
     check_attention(from_dev(out)[sample], lse.cpu().numpy()[sample], up, gi[sample].astype(np.int64), sample)
 
 
 def test_full_prefill64k_sampled(dsa_gpu):
+    """Boundary rows {0, 1, 2, k-2 .. k+1}, the last 64 rows and 256 seeded
+    random rows of the 64K prefill: scores (X12), selection and attention."""
     _say("[full] prefill64k sampled rows (streaming path)")
     wl = standard_workload("prefill64k")
     rng = np.random.default_rng(2)
     k = wl.topk
-    sample = np.unique(np.concatenate([[0, 1, 2, k - 2, k - 1, k, k + 1], np.arange(65536 - 8, 65536),
-                                       rng.choice(65536, 12, replace=False)]))
+    sample = np.unique(np.concatenate([[0, 1, 2, k - 2, k - 1, k, k + 1], np.arange(65536 - 64, 65536),
+                                       rng.choice(65536, 256, replace=False)]))
     up = Uploaded(wl, qm_rows=sample)
     g = up.geom(dsa_gpu)
     idx, out, lse = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
                                     index_k_scale=up.d_ks, want_lse=True)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()[sample]
-    ref = up.oracle_scores(rows=sample)
+    ref = _check_sampled_scores(dsa_gpu, up, g, sample)
     check_topk(gi, ref, wl.positions()[sample], k)
     check_attention(from_dev(out[torch.from_numpy(sample).cuda()]), lse.cpu().numpy()[sample], up,
                     gi.astype(np.int64), sample)
