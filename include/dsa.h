@@ -365,6 +365,30 @@ typedef enum {
 DSA_API size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t k,
                                   int which_call);
 
+/* dsa_forward with no workspace argument, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The scratch memory is a static
+ * device array of DSA_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU
+ * (held from library load until the process ends); the call itself allocates
+ * and frees nothing.  Arguments, results and errors as dsa_forward, minus
+ * (ws, ws_bytes); the work runs on the stream's device.  Returns
+ * DSA_ERR_WORKSPACE, before touching the device, when the call needs more
+ * scratch than that: dsa_forward_workspace_size(...) bytes, plus
+ * B*q_len*topk*4 rounded up to 256 when idx_out is NULL (decode steps fit,
+ * e.g. 16 x 2 queries at context 131072 or 64 x 1 at 32768 with topk 2048
+ * and 128 heads; long prefills do not).  Nothing in the array needs to start
+ * at zero (the path clears what it counts into), so a call is unaffected by
+ * what an earlier call left there.  Every call on one GPU shares that GPU's
+ * array: calls that can overlap in time on one GPU (other streams, other
+ * host threads) race and must be serialised by the caller. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+DSA_API dsa_status dsa_forward_noalloc(const dsa_geom* geom, int32_t H, int32_t topk, float sm_scale,
+                       const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                       const void* index_w, dsa_dtype index_w_dtype,
+                       const void* index_k, const float* index_k_scale,
+                       const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype,
+                       int32_t* idx_out, void* out, float* lse, hipStream_t stream);
+
 /* Static text for a status code. */
 DSA_API const char* dsa_status_string(dsa_status status);
 

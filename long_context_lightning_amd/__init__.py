@@ -73,6 +73,7 @@ def load(path=None):
         "dsa_indexer_kl": (i32, [gp, i32, f32, vp, vp, i32, vp, vp, i64, vp, i32, vp, vp, vp, sz, vp]),
         "dsa_indexer_kl_workspace_size": (sz, [i32, i32, i32, i32]),
         "dsa_workspace_size": (sz, [i32, i32, i32, i32, i32, ctypes.c_int]),
+        "dsa_forward_noalloc": (i32, [gp, i32, i32, f32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp]),
         "dsa_status_string": (ctypes.c_char_p, [i32]),
         "dsa_version": (ctypes.c_char_p, []),
     }
@@ -90,7 +91,9 @@ ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "d
                  "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
                  "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_mha_prefill",
                  "dsa_mha_prefill_workspace_size", "dsa_indexer_kl", "dsa_indexer_kl_workspace_size",
-                 "dsa_workspace_size", "dsa_status_string", "dsa_version")
+                 "dsa_workspace_size", "dsa_forward_noalloc", "dsa_status_string", "dsa_version")
+
+NOALLOC_SCRATCH_BYTES = 96 << 20   # DSA_NOALLOC_SCRATCH_BYTES
 
 # which_call values of dsa_workspace_size
 CALL_TOPK, CALL_SPARSE_MLA, CALL_FORWARD, CALL_SPARSE_MLA_PAGED, CALL_FORWARD_PAGED, CALL_MHA_PREFILL, \
@@ -317,6 +320,39 @@ def forward(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, in
         _check(lib.dsa_forward(ctypes.byref(geom), *args), "dsa_forward")
     else:
         _check(lib.dsa_forward_paged(ctypes.byref(geom), ctypes.byref(pages), *args), "dsa_forward_paged")
+    return idx, out, lse
+
+
+def forward_noalloc(geom, topk_k, sm_scale, index_q, index_w, index_k, mla_q, mla_kv, index_k_scale=None,
+                    index_q_scale=None, idx=None, out=None, lse=None, want_lse=True, stream=None):
+    """dsa_forward_noalloc: dsa_forward with the library's static scratch
+    instead of a workspace (pass preallocated idx / out / lse to allocate
+    nothing at all).  ``idx=False`` passes idx_out = NULL.  Returns (idx, out, lse)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    H = mla_q.shape[1]
+    dev = mla_q.device
+    no_idx = idx is False
+    if idx is None:
+        idx = torch.empty((T, topk_k), dtype=torch.int32, device=dev)
+    elif no_idx:
+        idx = None
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=mla_q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    for name, t in (("index_q", index_q), ("index_w", index_w), ("index_k", index_k), ("mla_q", mla_q),
+                    ("mla_kv", mla_kv), ("idx", idx), ("out", out)):
+        if t is not None:
+            _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == (geom.B, geom.S_max, 128),
+          "indexer shapes mismatch")
+    _need(tuple(mla_kv.shape) == (geom.B, geom.S_max, 576) and mla_q.shape[0] == T, "MLA shapes mismatch")
+    st = lib.dsa_forward_noalloc(ctypes.byref(geom), H, topk_k, float(sm_scale), _ptr(index_q), _index_dtype(index_q),
+                                 _ptr(index_q_scale), _ptr(index_w), _w_dtype(index_w), _ptr(index_k),
+                                 _ptr(index_k_scale), _ptr(mla_q), _ptr(mla_kv), _mla_dtype(mla_q), _ptr(idx),
+                                 _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "dsa_forward_noalloc")
     return idx, out, lse
 
 

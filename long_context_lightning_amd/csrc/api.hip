@@ -1,6 +1,9 @@
 // Host side of the C ABI declared in include/dsa.h: argument validation,
 // workspace carving and the order of launches.  No allocation, no
 // synchronisation, no exceptions across the boundary.
+#include <atomic>
+#include <mutex>
+
 #include "dsa_internal.h"
 
 namespace dsa {
@@ -371,6 +374,44 @@ dsa_status cache_append_impl(const dsa_geom* geom, const dsa_pages* pages, const
   return hip_status(launch_cache_append(a, k_dtype == DSA_BF16, stream));
 }
 
+// ---- scratch memory of dsa_forward_noalloc
+//
+// A static device array: every GPU the library runs on holds its own copy
+// from module load to process exit.  In host code `scratch` only names the
+// symbol; its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of device dev's copy of `scratch`.
+hipError_t scratch_address(int dev, void** addr) {
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = 0;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t back = hipSetDevice(cur);
+        if (e == hipSuccess) e = back;
+      }
+      if (e != hipSuccess) return e;
+      if (!p || ((uintptr_t)p & (kAlign - 1))) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -615,6 +656,25 @@ size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, in
       break;
   }
   return best;
+}
+
+dsa_status dsa_forward_noalloc(const dsa_geom* geom, int32_t H, int32_t topk, float sm_scale, const void* index_q,
+                               dsa_dtype index_dtype, const float* index_q_scale, const void* index_w,
+                               dsa_dtype index_w_dtype, const void* index_k, const float* index_k_scale,
+                               const void* mla_q, const void* mla_kv, dsa_dtype mla_dtype, int32_t* idx_out,
+                               void* out, float* lse, hipStream_t stream) {
+  if (!geom_ok(geom) || H < 1 || topk < 1) return DSA_ERR_INVALID_ARG;
+  size_t need = dsa_forward_workspace_size(geom->B, geom->q_len, geom->S_max, H, topk, index_dtype, mla_dtype);
+  if (!idx_out) need += align_up((size_t)rows_of(geom) * topk * sizeof(int32_t));
+  if (need > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) return DSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return DSA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (scratch_address(dev, &ws) != hipSuccess) return DSA_ERR_HIP;
+  return forward_impl(geom, nullptr, H, topk, sm_scale, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                      index_k, index_k_scale, mla_q, mla_kv, mla_dtype, idx_out, out, lse, ws,
+                      DSA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 const char* dsa_status_string(dsa_status s) {

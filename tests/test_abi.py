@@ -264,3 +264,18 @@ def test_single_workspace_query_covers_every_dtype():
     assert pre == max(lib.dsa_forward_workspace_size(1, 65536, 65536, 128, 2048, i, m) for i in (0, 2) for m in (0, 1))
     assert lib.dsa_workspace_size(B, q_len, S, H, k, 99) == 0
     assert lib.dsa_workspace_size(0, q_len, S, H, k, lcl.CALL_FORWARD) == 0
+
+
+def test_forward_noalloc_rejects_before_touching_the_device():
+    """dsa_forward_noalloc: a geometry whose workspace exceeds the static
+    scratch (an 8192-token prefill) and a missing geometry are rejected on
+    the host, with no device call (this process has none)."""
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    big = _geom(B=1, q_len=8192, S=8192)
+    assert lib.dsa_forward_workspace_size(1, 8192, 8192, 128, 2048, 2, 1) > lcl.NOALLOC_SCRATCH_BYTES
+    call = lambda g, H=128, k=2048: lib.dsa_forward_noalloc(g, H, k, 0.1, P(FAKE), 2, None, P(FAKE), 1, P(FAKE),
+                                                          None, P(FAKE), P(FAKE), 1, P(FAKE), P(FAKE), None, None)
+    assert call(ctypes.byref(big)) == 3
+    assert call(None) == 1
+    assert call(ctypes.byref(_geom(B=2, q_len=1, S=4096)), H=0) == 1
