@@ -270,7 +270,8 @@ DSA_API size_t dsa_sparse_mla_paged_workspace_size(int32_t B, int32_t q_len, int
 
 /* dsa_forward on paged caches (index_k_pool / index_k_scale_pool as in
  * dsa_indexer_scores_paged, mla_kv_pool as in dsa_sparse_mla_paged).
- * Every shape scores into the workspace (no streamed prefill).
+ * Long prefills stream as in dsa_forward (the key tiles are read from their
+ * pages); other shapes score into the workspace.
  * ws >= dsa_forward_paged_workspace_size(...) bytes. */
 DSA_API dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t topk,
                        float sm_scale,

@@ -174,9 +174,8 @@ MlaArgs make_mla_args(const dsa_geom* g, int32_t H, int32_t k, float sm_scale, c
   return a;
 }
 
-// Workspace plan of dsa_forward.
-// Paged caches always take the chunked (score buffer) path and add a buffer
-// for the translated pool rows of the selection.
+// Workspace plan of dsa_forward.  Paged caches add a buffer for the
+// translated pool rows of the selection.
 struct ForwardPlan {
   bool streaming;
   int chunk_rows;
@@ -187,7 +186,7 @@ ForwardPlan plan_forward(int B, int q_len, int S_max, int H, int topk, dsa_dtype
                          bool paged) {
   ForwardPlan p{};
   const long long T = (long long)B * q_len;
-  p.streaming = !paged && index_dt == DSA_FP8_E4M3FN && q_len >= 64 && prefill_supported(q_len, S_max, topk);
+  p.streaming = index_dt == DSA_FP8_E4M3FN && q_len >= 64 && prefill_supported(q_len, S_max, topk);
   size_t off = 0;
   if (p.streaming) {
     p.chunk_rows = 0;

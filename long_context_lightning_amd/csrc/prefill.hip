@@ -450,6 +450,7 @@ __device__ uint32_t wave_compact_lds(uint32_t* ekey, uint32_t* eidx, int& n, int
   return tau;
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
   constexpr int R = kRowsPerWave;
   // K tiles: 128-byte rows, the 16-byte chunk ch of key j at slot ch ^ (j & 7)
@@ -538,16 +539,37 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   // ahead: wave w moves keys 8w..8w+7 of a tile (lane l: key 8w + l/8, slot
   // l%8); wave 0 also moves the tile's 64 k-scales.  Keys past the last
   // row's position read that position's row (their scores are masked).
-  const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (size_t)b * a.S_max * kDI;
-  const float* ksb = a.k_scale ? a.k_scale + (size_t)b * a.S_max : nullptr;
+  const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (PAGED ? 0 : (size_t)b * a.S_max * kDI);
+  const float* ksb = a.k_scale ? a.k_scale + (PAGED ? 0 : (size_t)b * a.S_max) : nullptr;
   const int ntiles = (maxpos + kNK) / kNK;
   static_assert(kNK == 8 * kWaves, "one 16-byte copy per lane per tile");
+  // Paged caches: a page holds a power of two >= 64 tokens, so a 64-key
+  // tile lies inside one page.  Lane i holds the id of page 64*pbatch + i of
+  // this sequence (64 pages per batch, refilled when the tiles move past
+  // them); a tile's page is a readlane, so no table read sits in front of its
+  // copies except once per 64 pages.
+  int pbatch = -1, lane_page = 0;
+  const int last_j = PAGED ? maxpos >> a.pages.shift : 0;
+  auto tile_rows = [&](int ti) -> long long {  // pool row of key ti*kNK
+    if constexpr (PAGED) {
+      const int s0 = ti * kNK, j = s0 >> a.pages.shift;
+      if ((j >> 6) != pbatch) {
+        pbatch = j >> 6;
+        lane_page = a.pages.page(b, min(64 * pbatch + lane, last_j));
+      }
+      const int pg = __builtin_amdgcn_readlane(lane_page, j & 63);
+      return ((long long)pg << a.pages.shift) | (s0 & ((1 << a.pages.shift) - 1));
+    } else {
+      return (long long)ti * kNK;
+    }
+  };
   auto issue = [&](int ti, int buf) {
+    const long long row0 = tile_rows(ti);  // keys ti*kNK .. +63 are rows row0 .. +63
     const int key = ti * kNK + 8 * wave + (lane >> 3);
-    const int kc = min(key, maxpos);
+    const int kc = min(key, maxpos) - ti * kNK;
     const uint32_t chunk = (uint32_t)((lane & 7) ^ (key & 7));
-    dma16_lds(kb8, (uint32_t)kc * kDI + 16u * chunk, &ktile[buf][8 * wave * kDI]);
-    if (wave == 0 && ksb) dma4_lds(ksb, 4u * (uint32_t)min(ti * kNK + lane, maxpos), &ksc[buf][0]);
+    dma16_lds(kb8 + row0 * kDI, (uint32_t)kc * kDI + 16u * chunk, &ktile[buf][8 * wave * kDI]);
+    if (wave == 0 && ksb) dma4_lds(ksb + row0, 4u * (uint32_t)(min(ti * kNK + lane, maxpos) - ti * kNK), &ksc[buf][0]);
   };
 
   // A tile's accepted candidates are stored at the start of the next tile
@@ -699,7 +721,10 @@ size_t prefill_workspace_bytes(int B, int q_len, int S_max, int k) {
 hipError_t launch_indexer_topk_prefill(const IndexerArgs& a, int k, int32_t* idx, void* ws, hipStream_t stream) {
   const int nqb = (a.q_len + kRows - 1) / kRows;
   const dim3 grid((unsigned)(nqb * a.B));
-  hipLaunchKernelGGL(k_prefill, grid, dim3(kThreads), 0, stream, a, k, idx, ws, cand_cap(k));
+  if (a.pages.table)
+    hipLaunchKernelGGL(k_prefill<true>, grid, dim3(kThreads), 0, stream, a, k, idx, ws, cand_cap(k));
+  else
+    hipLaunchKernelGGL(k_prefill<false>, grid, dim3(kThreads), 0, stream, a, k, idx, ws, cand_cap(k));
   return hipGetLastError();
 }
 

@@ -174,9 +174,9 @@ def test_paged_validation():
                                                 wsb, None)
     assert fwd(None, fneed) == 1
     assert fwd(ok, fneed - 1) == 3
-    # a long prefill is never streamed when paged: the workspace holds the score chunk
+    # a long prefill streams when paged too: the streamed plan plus the translated rows, no score chunk
     pre = lib.dsa_forward_paged_workspace_size(1, 65536, 65536, 128, 2048, 2, 1)
-    assert pre >= (256 << 20) + 65536 * 2048 * 4                               # score chunk + translated rows
+    assert pre == lib.dsa_forward_workspace_size(1, 65536, 65536, 128, 2048, 2, 1) + 65536 * 2048 * 4
 
     app = lambda pg: lib.dsa_indexer_cache_append_paged(ctypes.byref(g), pg, P(FAKE), 1, P(FAKE), P(FAKE), None)
     assert app(None) == 1

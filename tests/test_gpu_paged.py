@@ -84,7 +84,8 @@ PAGED = [
     ("p64_ragged", 4, 1, [3000, 64, 1777, 129], 3000, 256, 32, 64, True, "normal", 0),
     ("p256_two_q_shared", 3, 2, [5000, 4097, 2], 5000, 512, 16, 256, True, "normal", 8),
     ("p8192_ties", 2, 2, [9000, 8193], 9000, 256, 16, 8192, True, "pool", 0),
-    ("p128_long_q", 1, 300, [700], 700, 128, 16, 128, True, "normal", 0),
+    ("p128_long_q", 1, 300, [700], 700, 128, 16, 128, True, "normal", 0),       # streamed prefill
+    ("p64_stream_two_seqs", 2, 600, [2600, 900], 2600, 256, 16, 64, True, "pool", 4),  # streamed, shared prefix
     ("p64_f32", 2, 20, [512, 100], 512, 64, 16, 64, False, "normal", 1),
     ("p64_keep_all", 2, 40, [300, 41], 300, 512, 16, 64, True, "normal", 0),   # S_max <= topk: indexer bypassed
     ("p64_long_and_short", 2, 1, [40000, 100], 40000, 256, 16, 64, True, "normal", 0),  # multi-launch top-k
@@ -212,3 +213,57 @@ def test_full_decode128k_paged(dsa_gpu):
     check_topk(gi[rows], ref, wl.positions()[rows], wl.topk)
     check_attention(from_dev(out_p)[rows], lse_p.cpu().numpy()[rows], _OracleView(wl, qm, kv),
                     gi[rows].astype(np.int64), rows)
+
+
+def _pools(lcl, clean, num_pages, P, caches):
+    """Device page pools holding the contiguous device caches [B, S, ...] at
+    the pages of ``clean`` (pool page clean[b, j] = tokens j*P.. of sequence b)."""
+    dst = torch.from_numpy(clean.reshape(-1).astype(np.int64)).cuda()
+    out = []
+    for c in caches:
+        tail = tuple(c.shape[2:])
+        out.append(torch.zeros((num_pages, P) + tail, dtype=c.dtype, device="cuda").index_copy_(
+            0, dst, c.reshape((-1, P) + tail)))
+    return out
+
+
+@pytest.mark.parametrize("name", ["prefill8k", "prefill64k"])
+def test_full_prefill_paged_streamed(dsa_gpu, name):
+    """The 8K (planted) and 64K prefills on 64-token pages stream their scores
+    like the contiguous forward (no T x S buffer in the paged workspace):
+    selection and attention bit-exact against the contiguous forward on the
+    same cache, the planted sets recovered, and the oracle's verdict on
+    sampled rows."""
+    lcl = dsa_gpu
+    _say(f"[paged] full {name}, 64-token pages, streamed")
+    wl = standard_workload(name)
+    L, k, P = wl.T, wl.topk, 64
+    rng = np.random.default_rng(12)
+    sample = np.unique(np.r_[[0, 1, k - 1, k, k + 1, L - 1], rng.choice(L, 10, replace=False)])
+    if wl.planted_rows is not None:
+        sample = np.unique(np.r_[sample, wl.planted_rows[:4]])
+    from tests.gpu_util import Uploaded
+    up = Uploaded(wl, qm_rows=sample)
+    table, clean, num_pages = make_block_table(14, wl.B, wl.seq_lens, wl.S_max, P)
+    ki_pool, ks_pool, kv_pool = _pools(lcl, clean, num_pages, P, (up.d_ki, up.d_ks, up.d_kv))
+    d_table = torch.from_numpy(table).cuda()
+    pages = lcl.make_pages(d_table, P, num_pages)
+    g = up.geom(lcl)
+    need_p = lcl.forward_paged_workspace_size(wl.B, L, wl.S_max, wl.H, k, lcl.FP8_E4M3FN, lcl.BF16)
+    need_c = lcl.forward_workspace_size(wl.B, L, wl.S_max, wl.H, k, lcl.FP8_E4M3FN, lcl.BF16)
+    assert need_p == need_c + (L * k * 4 + 255) // 256 * 256       # streamed: no score buffer
+    idx_p, out_p, lse_p = lcl.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, ki_pool, up.d_qm, kv_pool,
+                                      index_k_scale=ks_pool, pages=pages)
+    idx_c, out_c, lse_c = lcl.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
+                                      index_k_scale=up.d_ks)
+    torch.cuda.synchronize()
+    assert _same(idx_p, idx_c), "paged selection differs from the contiguous forward"
+    assert _same(out_p, out_c) and _same(lse_p, lse_c), "paged attention differs from the contiguous forward"
+    gi = idx_p.cpu().numpy()
+    if wl.planted_rows is not None:
+        for t in wl.planted_rows:
+            assert np.array_equal(gi[t], wl.planted_set), f"planted row {t} lost its planted set"
+    ref = up.oracle_scores(rows=sample)
+    check_topk(gi[sample], ref, wl.positions()[sample], k)
+    check_attention(from_dev(out_p[torch.from_numpy(sample).cuda()]), lse_p.cpu().numpy()[sample], up,
+                    gi[sample].astype(np.int64), sample)
