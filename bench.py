@@ -223,9 +223,10 @@ def main():
         prefill = bench_prefill(args, lcl, torch, np, dev, stream, evict)
 
     # ------------------------------------------------------ CPU baseline
-    cpu = None
+    cpu = cpu_other = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, qi, w, ki, ks, qm, np, args.cpu_seconds)
+        cpu_other = cpu_baseline_configs(np, args.cpu_seconds)
 
     line = {
         "metric": "DSA decode queries/s @128K ctx (dsa_forward: indexer + top-k + sparse MLA)",
@@ -253,6 +254,8 @@ def main():
         "other_configs": other,
         "prefill": prefill,
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_other,
+        "workspace_bytes": lcl.forward_workspace_size(wl.B, wl.q_len, wl.S_max, H, k, lcl.FP8_E4M3FN, lcl.BF16),
         "system": system_info(torch, lcl),
     }
     print(json.dumps(line), flush=True)
@@ -424,25 +427,61 @@ def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, 
     def fwd():
         lcl.forward(geom, k, sm, qi, w, ki, qm, kv, index_k_scale=ks, idx=idx, out=out, ws=ws, want_lse=False)
 
+    mla_ws = torch.empty(max(lcl.sparse_mla_workspace_size(B, q_len, H, k, lcl.BF16), 256), dtype=torch.uint8,
+                         device=dev)
+
+    def mla():
+        lcl.sparse_mla(geom, qm, kv, idx, sm, out=out, ws=mla_ws, want_lse=False)
+
     for _ in range(2):
         evict()
         fwd()
-    ts = []
+    ts, tm = [], []
     for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         evict()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record(stream)
         fwd()
         e[1].record(stream)
+        evict()
+        e[2].record(stream)
+        mla()
+        e[3].record(stream)
         torch.cuda.synchronize()
         ts.append(e[0].elapsed_time(e[1]))
+        tm.append(e[2].elapsed_time(e[3]))
     ms = sum(ts) / len(ts)
+    mla_ms = sum(tm) / len(tm)
     rate = T / (ms * 1e-3)
-    log(f"{label}: {ms * 1e3:.1f} us/step -> {rate:,.0f} {unit}")
-    del qi, ki, ks, w, qm, kv, idx, out, ws
+    # roofline of the whole step: decode shapes against the HBM floor of the
+    # algorithmic bytes, prefill shapes against the MFMA floor of the
+    # algorithmic flops (indexer fp8, attention bf16)
+    sel = sum(min(t + 1, k) for t in range(S - q_len, S)) * B
+    if q_len == 1:
+        idx_bytes = B * S * (128 + 4)
+        mla_bytes = sel * 1152 + T * H * 576 * 2 + T * H * 512 * 2 + T * k * 4
+        floor_us = (idx_bytes + T * S * 4 + mla_bytes) / (HBM_PEAK_GBS * 1e3)
+        roof = {"bound": "hbm", "algorithmic_bytes": idx_bytes + T * S * 4 + mla_bytes,
+                "floor_us": round(floor_us, 2), "frac": round(floor_us / (ms * 1e3), 4),
+                "sparse_mla_us": round(mla_ms * 1e3, 2),
+                "sparse_mla_hbm_frac": round(mla_bytes / (mla_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        pairs = B * q_len * (q_len + 1) // 2
+        idx_flop, mla_flop = pairs * 64 * 128 * 2, sel * H * (576 + 512) * 2
+        floor_ms = idx_flop / (FP8_PEAK_TFLOPS * 1e9) + mla_flop / (BF16_PEAK_TFLOPS * 1e9)
+        i_ms = max(ms - mla_ms, 1e-6)
+        roof = {"bound": "mfma", "indexer_tflop": round(idx_flop / 1e12, 4), "sparse_mla_tflop": round(mla_flop / 1e12, 4),
+                "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms, 4),
+                "indexer_topk_ms": round(i_ms, 3),
+                "indexer_fp8_mfma_frac": round(idx_flop / (i_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                "sparse_mla_ms": round(mla_ms, 3),
+                "sparse_mla_bf16_mfma_frac": round(mla_flop / (mla_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    log(f"{label}: {ms * 1e3:.1f} us/step -> {rate:,.0f} {unit}; roofline frac {roof['frac']:.3f} ({roof['bound']})")
+    del qi, ki, ks, w, qm, kv, idx, out, ws, mla_ws
     torch.cuda.empty_cache()
     return {"workload": label, "us_per_step": round(ms * 1e3, 2), "value": round(rate, 1), "unit": unit,
-            "steps": steps}
+            "steps": steps, "roofline": roof,
+            "workspace_bytes": lcl.forward_workspace_size(B, q_len, S, H, k, lcl.FP8_E4M3FN, lcl.BF16)}
 
 
 def bench_kl(lcl, torch, dev, stream, evict, steps=5):
@@ -611,6 +650,33 @@ def bench_prefill(args, lcl, torch, np, dev, stream, evict):
     f_ms = sum(fwd_ms) / len(fwd_ms)
     m_ms = sum(mla_ms) / len(mla_ms)
     i_ms = max(f_ms - m_ms, 1e-6)
+    # the same prefill on 64-token pages (scattered seeded table): it streams too
+    from synth import make_block_table
+    P = 64
+    table, clean, num_pages = make_block_table(10, 1, np.array([L]), L, P)
+    dst = torch.from_numpy(clean.reshape(-1).astype(np.int64)).to(dev)
+
+    def pool(c, tail):
+        return torch.zeros((num_pages, P) + tail, dtype=c.dtype, device=dev).index_copy_(0, dst, c.reshape((-1, P) + tail))
+
+    ki_p, ks_p, kv_p = pool(ki.view(torch.uint8), (128,)), pool(ks, ()), pool(kv, (576,))
+    pages = lcl.make_pages(torch.from_numpy(table).to(dev), P, num_pages)
+    pws = torch.empty(lcl.forward_paged_workspace_size(1, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16), dtype=torch.uint8,
+                      device=dev)
+    paged_ms = []
+    for i in range(2):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        evict()
+        e[0].record(stream)
+        lcl.forward(geom, k, sm, qi, w, ki_p, qm, kv_p, index_k_scale=ks_p, idx=idx, out=out, ws=pws, want_lse=False,
+                    pages=pages)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        if i >= 1:
+            paged_ms.append(e[0].elapsed_time(e[1]))
+    p_ms = sum(paged_ms) / len(paged_ms)
+    log(f"prefill on 64-token pages: {p_ms:.2f} ms ({p_ms / f_ms:.3f}x the contiguous forward)")
+    del ki_p, ks_p, kv_p, pws
     pairs = L * (L + 1) // 2
     idx_tflops = pairs * 64 * 128 * 2 / (i_ms * 1e-3) / 1e12
     sel_rows = sum(min(t + 1, k) for t in range(L))
@@ -624,6 +690,9 @@ def bench_prefill(args, lcl, torch, np, dev, stream, evict):
            "indexer_fp8_mfma_frac": round(idx_tflops / FP8_PEAK_TFLOPS, 4),
            "sparse_mla_ms": round(m_ms, 3), "sparse_mla_tflops": round(mla_tflops, 1),
            "sparse_mla_bf16_mfma_frac": round(mla_tflops / BF16_PEAK_TFLOPS, 4),
+           "paged_64_token_pages": {"ms_per_step": round(p_ms, 3), "tokens_per_s": round(L / (p_ms * 1e-3), 1),
+                                    "vs_contiguous": round(p_ms / f_ms, 4)},
+           "workspace_bytes": lcl.forward_workspace_size(1, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16),
            "data": "synthetic, drawn on the GPU with torch's seeded generator (same recipe)"}
     del qi, ki, ks, w, qm, kv, idx, out, ws
     torch.cuda.empty_cache()
@@ -652,6 +721,75 @@ def cpu_baseline(wl, qi, w, ki, ks, qm, np, budget_s):
     return {"value": round(nq / spent, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
             "sample": f"{nq} queries ({nseq} of the {wl.B} sequences x {wl.q_len}) of the 128K decode workload, "
                       f"all three stages in float64 NumPy, {spent:.1f}s"}
+
+
+def _oracle_rows(oracle, np, wl, rows, qi, w, ki, ks, qm, kv):
+    """The oracle's three stages for the given query rows (time in seconds)."""
+    t0 = time.perf_counter()
+    oracle.dsa_forward(qi, "e4m3fn", w, "bf16", ki, "e4m3fn", qm, "bf16", kv, "bf16", wl.seq_lens, wl.q_len, wl.topk,
+                       wl.sm_scale, k_scale=ks, rows=rows)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_configs(np, budget_s):
+    """The float64 oracle on the other fp8 configurations, each on a bounded
+    sample (about budget_s / 3 seconds each), on the host cores:
+      decode32k   whole sequences (one query each), queries/s;
+      prefill8k   the 32 planted rows plus 32 seeded uniformly random rows:
+                  rows/s on the sample, and the full 8192-row run
+                  extrapolated from the random rows (mean time per row x L);
+      prefill64k  seeded uniformly random rows, same report.
+    Inputs follow the same recipe (synth); only the sampled rows' queries
+    are drawn."""
+    import oracle
+    from synth import standard_workload
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+    wl = standard_workload("decode32k")
+    log(f"cpu baseline (configs): {wl.name}")
+    spent, n = 0.0, 0
+    while n < wl.B and (n == 0 or spent < budget_s / 3):
+        rows = np.array([n])
+        ki, ks = wl.ki(n)
+        # sequence n as a B = 1 geometry of the same recipe
+        sub = type(wl)(name=wl.name, B=1, q_len=1, S_max=wl.S_max, seq_lens=wl.seq_lens[n:n + 1], topk=wl.topk,
+                       H=wl.H, seed=wl.seed)
+        spent += _oracle_rows(oracle, np, sub, np.array([0]), wl.qi(rows), wl.w(rows), ki[None], ks[None], wl.qm(rows),
+                              wl.kv(n)[None])
+        n += 1
+    res["decode32k"] = {"value": round(n / spent, 4), "unit": "queries/s", "cores": cores, "kind": "oracle",
+                        "sample": f"{n} of the 64 sequences (1 query each), all three stages, {spent:.1f}s"}
+    for name, n_rand in (("prefill8k", 32), ("prefill64k", 12)):
+        wl = standard_workload(name)
+        log(f"cpu baseline (configs): {wl.name}")
+        L = wl.T
+        rng = np.random.default_rng(17)
+        rand = np.sort(rng.choice(L, n_rand, replace=False))
+        planted = wl.planted_rows if wl.planted_rows is not None else np.array([], np.int64)
+        sample = np.unique(np.concatenate([planted, rand]))
+        qi = np.zeros((L, 64, 128), np.uint8)
+        qi[sample] = wl.qi(sample)
+        w = wl.w()
+        qm = np.zeros((L, wl.H, 576), np.uint16)
+        qm[sample] = wl.qm(sample)
+        ki, ks = wl.ki_all()
+        kv = wl.kv_all()
+        t_rand = 0.0
+        for t in rand:
+            t_rand += _oracle_rows(oracle, np, wl, np.array([t]), qi, w, ki, ks, qm, kv)
+        t_all = t_rand
+        others = np.setdiff1d(sample, rand)
+        if len(others):
+            t_all += _oracle_rows(oracle, np, wl, others, qi, w, ki, ks, qm, kv)
+        extrap = t_rand / len(rand) * L
+        res[name] = {"value": round(len(sample) / t_all, 4), "unit": "tokens/s (sampled rows)", "cores": cores,
+                     "kind": "oracle",
+                     "sample": f"{len(sample)} query rows ({len(planted)} planted, {len(rand)} seeded uniform random) "
+                               f"of the {L}-token prefill, all three stages, {t_all:.1f}s",
+                     "extrapolated_full_run_s": round(extrap, 1),
+                     "extrapolated_note": "mean oracle time of the uniform random rows x L (an estimate, not a run)"}
+        del qi, qm, kv
+    return res
 
 
 if __name__ == "__main__":
