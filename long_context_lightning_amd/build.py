@@ -42,6 +42,54 @@ def hipcc():
     return exe
 
 
+def m0_violations(asm_text):
+    """Lines of gfx950 device assembly that reference m0 outside an inline
+    asm block.  The LDS-DMA helpers (dsa_internal.h) set m0 from inline asm
+    right before each global_load_lds; the backend treats m0 as reserved and
+    does not honour a clobber of it, so the kernels stay correct only while the
+    compiler itself never reads or writes m0 in them (no LDS-DMA builtin,
+    s_sendmsg, relative register moves, ...)."""
+    import re
+    implicit = re.compile(r"^\s*(v_movrel|s_movrel|s_sendmsg|v_interp|ds_gws|ds_append|ds_consume|ds_ordered_count|"
+                          r"global_load_lds|buffer_load\S*\s.*\blds\b)")
+    bad, in_asm = [], False
+    for n, line in enumerate(asm_text.splitlines(), 1):
+        if ";;#ASMSTART" in line:
+            in_asm = True
+        elif ";;#ASMEND" in line:
+            in_asm = False
+        else:
+            code = line.split(";")[0]
+            if not in_asm and ("m0" in code.replace(",", " ").split() or implicit.match(code)):
+                bad.append((n, line.strip()))
+    return bad
+
+
+def check_m0(verbose=False):
+    """Compile every source to gfx950 device assembly and fail if the
+    compiler references m0 anywhere outside the inline asm blocks."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(src):
+        with tempfile.TemporaryDirectory() as d:
+            out = os.path.join(d, src + ".s")
+            cmd = [hipcc(), *[f for f in FLAGS if f not in ("-shared", "-fPIC")], "--cuda-device-only", "-S",
+                   "-I", INCLUDE, "-I", CSRC, os.path.join(CSRC, src), "-o", out]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise subprocess.CalledProcessError(res.returncode, cmd, res.stdout, res.stderr)
+            return src, m0_violations(open(out).read())
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        found = [r for r in ex.map(one, SOURCES) if r[1]]
+    if found:
+        msg = "; ".join(f"{src}: line {n}: {text}" for src, lines in found for n, text in lines[:3])
+        raise RuntimeError(f"compiler-generated m0 use next to the inline-asm LDS copies: {msg}")
+    if verbose:
+        print(f"m0 check: no compiler use of m0 in {len(SOURCES)} sources", flush=True)
+
+
 def build(verbose=False, extra_flags=()):
     """Compile libdsa.so; raises CalledProcessError on failure."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
@@ -58,6 +106,7 @@ def build(verbose=False, extra_flags=()):
     if verbose and err.strip():
         sys.stderr.write(err + "\n")
     os.replace(tmp, LIB)
+    check_m0(verbose)
     return LIB
 
 
