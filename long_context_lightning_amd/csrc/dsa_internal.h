@@ -171,6 +171,17 @@ __device__ __forceinline__ void dma16_lds_at(const void* gaddr, uint32_t lds_off
 }
 #pragma clang diagnostic pop
 
+// As dma16_lds, with the LDS destination given as a byte offset (the same
+// for every lane of the wave).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_lds_off(const void* gbase, uint32_t voff, uint32_t lds_off) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_off);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(gbase), "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // LDS byte offset of a __shared__ object (its address in the LDS aperture).
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_void_t*)p;

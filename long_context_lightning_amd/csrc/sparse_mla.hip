@@ -45,6 +45,7 @@ constexpr int kRopeRS = 128;                     // dims 512..575 of a row: 8 pi
 constexpr int kTileBytes = kMainBytes + kNT * kRopeRS;  // 37888
 constexpr int kWaves = 4;                        // one per SIMD
 constexpr int kSlots = 4;                        // ring slots: values, scores, two tiles in flight
+constexpr int kISlots = 4;                       // index slots per wave (indices arrive four tiles ahead)
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = kNT / kWaves;       // rows of a tile gathered by each wave (8)
 constexpr int kDma = kRowsPerWave + 1;           // gather instructions per wave per tile
@@ -135,56 +136,61 @@ struct TileSrc {
   int m1, pos;
 };
 
-// The gather of one tile in steps, so the tile loop can spread them over
-// the score MFMAs of the tile before (their issue costs then overlap matrix
-// work): the wave's eight indices (from LDS, or from a scalar load before the
-// loop), their validity, then one instruction per row and the rope one.
+// The gather of one tile: prepare() takes the wave's eight indices (one per
+// lane group: lane l works on row l & 7, and on row l >> 3 for the rope
+// instruction) and their validity (one ballot gives the tile's mask byte),
+// in vector registers, and leaves the row to read per lane (row 0 for an
+// invalid entry); issue() takes each row's index from lane rr (a readlane),
+// forms its base address in scalar registers and issues the nine copies.
+// A copy instruction into LDS takes far longer to issue than the scalar
+// arithmetic between two of them, and no compare/select chain per row sits
+// in the issue stream.
 struct TileGather {
-  v4i lo, hi;                 // raw indices of rows 0..3 / 4..7 (the same in every lane)
-  int sidx[kRowsPerWave];     // rows to read (0 for invalid ones), held per lane
-  int rope_s;                 // this lane's row of the rope instruction
-  uint32_t lane16;            // 16 * lane, made opaque per tile so no per-row address is hoisted
+  v4i lo, hi;         // raw indices of rows 0..3 / 4..7 (uniform; before the tile loop only)
+  int raw, rraw;      // lane l: index of row l & 7 / of row l >> 3 (0 when invalid, after prepare)
 
-  __device__ __forceinline__ void read_lds(const int32_t* slot) {
-    lo = *reinterpret_cast<const v4i*>(slot);
-    hi = *reinterpret_cast<const v4i*>(slot + 4);
+  // indices of the eight rows from the wave's LDS slot (inside the tile loop)
+  __device__ __forceinline__ void read_lds(const int32_t* slot, int lane) {
+    raw = slot[lane & 7];
+    rraw = slot[lane >> 3];
   }
-  // Validity of the wave's rows (entries at or past the split end, negative
-  // or past the query position are invalid), computed per lane on vectors so
-  // no scalar chain sits in the issue stream.
-  __device__ __forceinline__ void decode(const TileSrc& src, int mb, unsigned char* vmask, int wave, int lane) {
-    const int mw = mb + wave * kRowsPerWave;
-    uint32_t vbits = 0;
+  // ... or from the uniform values of a scalar load (before the loop)
+  __device__ __forceinline__ void from_uniform(int lane) {
+    const int i = lane & 7, j = lane >> 3;
+    raw = lo[0];
+    rraw = lo[0];
 #pragma unroll
-    for (int rr = 0; rr < kRowsPerWave; ++rr) {
-      const int raw = rr < 4 ? lo[rr] : hi[rr - 4];
-      const bool ok = mw + rr < src.m1 && raw >= 0 && raw <= src.pos;
-      sidx[rr] = ok ? raw : 0;
-      vbits |= (ok ? 1u : 0u) << rr;
+    for (int rr = 1; rr < kRowsPerWave; ++rr) {
+      const int v = rr < 4 ? lo[rr] : hi[rr - 4];
+      raw = i == rr ? v : raw;
+      rraw = j == rr ? v : rraw;
     }
-    if (lane == 0) vmask[wave] = (unsigned char)vbits;  // byte w: validity of rows 8w..8w+7
-    lane16 = 16u * (uint32_t)lane;
-    asm volatile("" : "+v"(lane16));
-    const int rr = lane >> 3;
-    rope_s = sidx[0];
-#pragma unroll
-    for (int j = 1; j < kRowsPerWave; ++j) rope_s = rr == j ? sidx[j] : rope_s;
   }
-  // dims 0..511 of tile row 8w + rr: 64 pieces, one per lane (per-lane
-  // address: one multiply-add per row)
-  __device__ __forceinline__ void row(const TileSrc& src, int rr, uint32_t tile, int wave, int lane) const {
-    const char* rowp = reinterpret_cast<const char*>(src.kvb) + (size_t)sidx[rr] * (2 * kDQK);
-    dma16_lds_at(rowp + lane16, tile + (wave * kRowsPerWave + rr) * kMainRS);
+  // Validity (entries at or past the split end, negative or past the query
+  // position are invalid); byte w of vmask gets the validity of rows 8w..8w+7.
+  __device__ __forceinline__ void prepare(const TileSrc& src, int mb, unsigned char* vmask, int wave, int lane) {
+    const int mw = mb + wave * kRowsPerWave;
+    const bool ok = mw + (lane & 7) < src.m1 && raw >= 0 && raw <= src.pos;
+    const bool okr = mw + (lane >> 3) < src.m1 && rraw >= 0 && rraw <= src.pos;
+    const uint32_t vbits = (uint32_t)__ballot(ok) & 0xFFu;  // lanes 0..7: rows 0..7
+    if (lane == 0) vmask[wave] = (unsigned char)vbits;
+    raw = ok ? raw : 0;
+    rraw = okr ? rraw : 0;
+  }
+  // dims 0..511 of tile row 8w + rr (64 pieces; lane16 = 16 * lane)
+  __device__ __forceinline__ void row(const TileSrc& src, int rr, uint32_t tile, int wave, uint32_t lane16) const {
+    const int s = __builtin_amdgcn_readlane(raw, rr);
+    dma16_lds_off(src.kvb + (size_t)s * kDQK, lane16, tile + (wave * kRowsPerWave + rr) * kMainRS);
   }
   // rope pieces: lane l -> row 8w + l/8, slot l%8
   __device__ __forceinline__ void rope(const TileSrc& src, uint32_t tile, int wave, int lane) const {
     const int row0 = wave * kRowsPerWave;
     const int piece = 64 + ((lane & 7) ^ (((row0 + (lane >> 3)) >> 1) & 7));
-    dma16_lds_at(src.kvb + (size_t)rope_s * kDQK + 8 * piece, tile + kMainBytes + row0 * kRopeRS);
+    dma16_lds_at(src.kvb + (size_t)rraw * kDQK + 8 * piece, tile + kMainBytes + row0 * kRopeRS);
   }
-  __device__ __forceinline__ void all_rows(const TileSrc& src, uint32_t tile, int wave, int lane) const {
+  __device__ __forceinline__ void issue(const TileSrc& src, uint32_t tile, int wave, int lane, uint32_t lane16) const {
 #pragma unroll
-    for (int rr = 0; rr < kRowsPerWave; ++rr) row(src, rr, tile, wave, lane);
+    for (int rr = 0; rr < kRowsPerWave; ++rr) row(src, rr, tile, wave, lane16);
     rope(src, tile, wave, lane);
   }
 };
@@ -216,6 +222,7 @@ __device__ __forceinline__ TileGather scalar_indices(const TileSrc& src, int mb,
 // global -> LDS copy of the wave's eight entries (clamped into the split),
 // so no scalar-load latency sits in front of a gather.
 __device__ __forceinline__ void fetch_indices(const TileSrc& src, int mb, int32_t* slot, int wave, int lane) {
+  asm volatile("" : "+v"(lane));  // formed here, not hoisted out of the loops (it would be spilled)
   if (lane < kRowsPerWave) {
     const int m = mb + wave * kRowsPerWave + lane;
     dma4_lds(src.idx_row, 4u * (uint32_t)(m < src.m1 ? m : src.m1 - 1), slot);
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   // fall on distinct banks.
   __shared__ __attribute__((aligned(16))) unsigned char pbuf[kMaxHB * 16 * kPRow];
   __shared__ uint32_t vmask[kSlots];  // per ring slot: bit r = validity of tile row r
-  __shared__ __attribute__((aligned(16))) int32_t islot[kWaves][4][kRowsPerWave];  // prefetched row indices
+  __shared__ __attribute__((aligned(16))) int32_t islot[kWaves][kISlots][kRowsPerWave];  // prefetched row indices
   __shared__ float hinv[kMaxHB * 16];
   __shared__ int overflow_flag;
 
@@ -265,7 +272,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   int roff1 = roff0 ^ 64;  // rope piece 4 + g: slot (g ^ ((c >> 1) & 7)) ^ 4
   int voff = (4 * g + (c >> 2)) * kMainRS + 8 * (c & 3) + 2 * (kDV / kWaves) * wave;
   int poff = c * kPRow + 16 * (g ^ ((c >> 2) & 3));
-  asm volatile("" : "+v"(aoff), "+v"(roff0), "+v"(roff1), "+v"(voff), "+v"(poff));
+  // 16 * lane: the per-lane offset of every row copy (opaque, so no per-row
+  // address is formed ahead of time)
+  uint32_t lane16 = 16u * (uint32_t)lane;
+  asm volatile("" : "+v"(aoff), "+v"(roff0), "+v"(roff1), "+v"(voff), "+v"(poff), "+v"(lane16));
 
   TileSrc src;
   src.kvb = static_cast<const uint16_t*>(a.kv) + (a.flat ? 0 : (size_t)b * a.S_max * kDQK);
@@ -286,19 +296,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
     if (ntiles > 1) g1 = scalar_indices(src, m0 + kNT, wave);
     if (ntiles > 2) g2 = scalar_indices(src, m0 + 2 * kNT, wave);
     if (ntiles > 0) {
-      g0.decode(src, m0, vmb, wave, lane);
-      g0.all_rows(src, ring_off, wave, lane);
+      g0.from_uniform(lane);
+      g0.prepare(src, m0, vmb, wave, lane);
+      g0.issue(src, ring_off, wave, lane, lane16);
     }
   };
   auto prologue_rest = [&]() {
     if (ntiles > 1) {
-      g1.decode(src, m0 + kNT, vmb + 4, wave, lane);
-      g1.all_rows(src, ring_off + kTileBytes, wave, lane);
+      g1.from_uniform(lane);
+      g1.prepare(src, m0 + kNT, vmb + 4, wave, lane);
+      g1.issue(src, ring_off + kTileBytes, wave, lane, lane16);
     }
     if (ntiles > 3) fetch_indices(src, m0 + 3 * kNT, islot[wave][3], wave, lane);
     if (ntiles > 2) {
-      g2.decode(src, m0 + 2 * kNT, vmb + 8, wave, lane);
-      g2.all_rows(src, ring_off + 2 * kTileBytes, wave, lane);
+      g2.from_uniform(lane);
+      g2.prepare(src, m0 + 2 * kNT, vmb + 8, wave, lane);
+      g2.issue(src, ring_off + 2 * kTileBytes, wave, lane, lane16);
     }
   };
   prologue();
@@ -360,19 +373,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   // 16*kb + 4g + i; masked keys become -inf through a bit select.
   constexpr int kSoftSteps = 19;
   uint32_t vml;  // validity bits shifted so bit 16*kb + i is key 16*kb + 4g + i
+  bool vfull;    // every key of the tile is valid (the common case: no masking)
   float sv[8], tmax, nmr;
   uint32_t pk[4];
   auto soft_step = [&](int k, const v4f (&sa)[2][2], uint32_t vm) {
     if (k == 0) {
       vml = vm >> (4 * g);
+      vfull = vm == 0xFFFFFFFFu;
       return;
     }
     const int hb = (k - 1) / 9, st = (k - 1) % 9;
     if (hb == 1 && !sh1) return;
     if (st == 0) {
+      if (vfull) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        sv[j] = (vml >> (16 * (j >> 2) + (j & 3))) & 1u ? sa[j >> 2][hb][j & 3] : -INFINITY;
+        for (int j = 0; j < 8; ++j) sv[j] = sa[j >> 2][hb][j & 3];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          sv[j] = (vml >> (16 * (j >> 2) + (j & 3))) & 1u ? sa[j >> 2][hb][j & 3] : -INFINITY;
+      }
     } else if (st == 1) {
       tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     } else if (st == 2) {
@@ -394,9 +414,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[2 * j + 1], qk_scale, nmr));
       pk[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){p0, p1}, v2bf));
     } else {
+      // sum of the rounded weights, a pair per dot instruction (exact products by one)
       float psum = 0.f;
+      const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) psum += __uint_as_float(pk[j] << 16) + __uint_as_float(pk[j] & 0xFFFF0000u);
+      for (int j = 0; j < 4; ++j) psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[j]), ones, psum, false);
       l_part[hb] += psum;
       *reinterpret_cast<v4i*>(pbuf + (16 * (2 * wave + hb)) * kPRow + poff) =
           v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -405,21 +427,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   // O^T[dims, heads] += V^T[dims, keys] . P^T[keys, heads].  V^T fragments
   // (16 dims x keys {4g..4g+3, 16+4g..16+4g+3} for lane row g) are two LDS
   // transpose loads each: lane j of a 16-lane row supplies key kbase + j/4,
-  // dims 16db + 4*(j%4) .. +3.
+  // dims 16db + 4*(j%4) .. +3.  The first kVAhead fragments are read before
+  // the barrier that publishes P (values_pre).
+  constexpr int kVAhead = 3;
+  v4s vlo[kVAhead], vhi[kVAhead];
+  auto vaddr = [&](const unsigned char* tb, int db) { return tb + voff + 32 * db; };  // rows + 16: 16 * kMainRS further
+  auto values_pre = [&](const unsigned char* tb) {
+#pragma unroll
+    for (int db = 0; db < kVAhead; ++db) {
+      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(tb, db));
+      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(tb, db) + 16 * kMainRS));
+    }
+  };
   auto values = [&](const unsigned char* tb) {
     v8bf pf[kMaxHB];
 #pragma unroll
     for (int hb = 0; hb < kMaxHB; ++hb)
       if (hb < NHB) pf[hb] = as_v8bf(*reinterpret_cast<const v4i*>(pbuf + 16 * hb * kPRow + poff));
-    const unsigned char* v0 = tb + voff;
-    auto vaddr = [&](int db) { return v0 + 32 * db; };  // rows + 16: 16 * kMainRS further
-    constexpr int kVAhead = 3;
-    v4s vlo[kVAhead], vhi[kVAhead];
-#pragma unroll
-    for (int db = 0; db < kVAhead; ++db) {
-      vlo[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(db));
-      vhi[db] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(db) + 16 * kMainRS));
-    }
 #pragma unroll
     for (int db = 0; db < kDbW; ++db) {
       __builtin_amdgcn_sched_barrier(0);
@@ -430,8 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       for (int hb = 0; hb < kMaxHB; ++hb)
         if (hb < NHB) acc_o[db][hb] = mfma_bf16(av, pf[hb], acc_o[db][hb]);
       if (db + kVAhead < kDbW) {
-        vlo[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(db + kVAhead));
-        vhi[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(db + kVAhead) + 16 * kMainRS));
+        vlo[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)vaddr(tb, db + kVAhead));
+        vhi[sl] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vaddr(tb, db + kVAhead) + 16 * kMainRS));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -464,22 +488,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
     // (all shares landed; everyone is done with tile tt-1 and with the P
     // buffer), copy burst (indices of tile tt+4, rows of tile tt+3 into the
     // slot tile tt-1 used), scores of tile tt+1 interleaved with the softmax
-    // of tile tt, barrier (P complete), values of tile tt.  Per wave the
-    // copies go out in the order ..., idx(tt+3), rows(tt+2), idx(tt+4),
-    // rows(tt+3), so at most kDma copies in flight means rows(tt+1) and
-    // idx(tt+3) landed.
+    // of tile tt, the first V^T reads, barrier (P complete), values of tile
+    // tt.  Per wave the copies go out in the order ..., idx(tt+3), rows(tt+2),
+    // idx(tt+4), rows(tt+3), so at most kDma copies in flight means rows(tt+1)
+    // and idx(tt+3) landed.
     for (int tt = 0; tt < ntiles; ++tt) {
       if (tt + 2 < ntiles)
         vm_wait<kDma>();
       else
         vm_wait<0>();
       lds_barrier();
-      if (tt + 4 < ntiles) fetch_indices(src, m0 + (tt + 4) * kNT, islot[wave][(tt + 4) & 3], wave, lane);
+      if (tt + 4 < ntiles) fetch_indices(src, m0 + (tt + 4) * kNT, islot[wave][(tt + 4) % kISlots], wave, lane);
       if (tt + 3 < ntiles) {
         TileGather tg;
-        tg.read_lds(islot[wave][(tt + 3) & 3]);
-        tg.decode(src, m0 + (tt + 3) * kNT, vmb + 4 * ((tt + 3) & 3), wave, lane);
-        tg.all_rows(src, ring_off + ((tt + 3) & 3) * kTileBytes, wave, lane);
+        tg.read_lds(islot[wave][(tt + 3) % kISlots], lane);
+        tg.prepare(src, m0 + (tt + 3) * kNT, vmb + 4 * ((tt + 3) & 3), wave, lane);
+        tg.issue(src, ring_off + ((tt + 3) & 3) * kTileBytes, wave, lane, lane16);
       }
       if (sh0) {
         const uint32_t vm = vmask[tt & 3];
@@ -499,6 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
           for (int k = 0; k < kSoftSteps; ++k) soft_step(k, sacc, vm);
         }
       }
+      values_pre(ring + (tt & 3) * kTileBytes);
       lds_barrier();  // P of every head is in LDS
       values(ring + (tt & 3) * kTileBytes);
     }
