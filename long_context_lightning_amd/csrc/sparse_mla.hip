@@ -6,7 +6,8 @@
 // value its first 512 dims; the softmax covers the selected rows only.
 //
 // bf16 path.  A block owns one query row, one contiguous slice (split) of its
-// selected indices and all H heads, with 4 waves, one per SIMD (each wave has
+// selected indices and all H heads (or, for launches with few query rows,
+// one 64-head half of them: see launch_mla_bf16), with 4 waves, one per SIMD (each wave has
 // the SIMD's whole register file: 256 VGPRs plus 256 AGPRs).  The selected
 // rows are gathered 32 at a time (1152 bytes each, in 16-byte pieces,
 // straight from global memory into LDS) through a ring of three padded tiles,
@@ -105,6 +106,19 @@ __host__ __device__ inline int mla_splits(int T, int k) {
 __host__ __device__ inline int mla_per_split(int k, int ns) {
   int per = (k + ns - 1) / ns;
   return (per + kNT - 1) / kNT * kNT;
+}
+
+// Decomposition of one launch: ns splits per row and nh blocks per
+// (row, split).  With 128 heads and too few rows to fill the chip with one
+// split each, every (row, split) gets two 64-head blocks, so the same block
+// count needs half the splits (and half the split partials).
+struct MlaPlan {
+  int ns, nh;
+};
+__host__ inline MlaPlan mla_plan(int T, int H, int k) {
+  const int ns1 = mla_splits(T, k);
+  if (H == 128 && ns1 > 1) return MlaPlan{mla_splits(2 * T, k), 2};
+  return MlaPlan{ns1, 1};
 }
 
 struct Partials {
@@ -230,11 +244,17 @@ __device__ __forceinline__ void fetch_indices(const TileSrc& src, int mb, int32_
 }
 
 
-// NHB = H / 16 head blocks: wave w runs the softmax of blocks 2w and 2w+1
-// (those below NHB), and every wave's value product covers all NHB.
-template <int NHB>
+// NHB 16-head blocks per block; wave w runs the scores and softmax of blocks
+// SHB*w .. SHB*w + SHB-1 (those below NHB), and every wave's value product
+// covers all NHB.  SHB = 2: all H heads per block (NHB = H / 16).  SHB = 1:
+// a 64-head half per block (NHB = 4, one score block per wave), nh = 2 blocks
+// per (row, split), so a launch with few rows fills the chip with half the
+// splits (half the split partials).
+template <int NHB, int SHB>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32_t* __restrict__ idx, int ns,
                                                         int per_split, int per_xcd) {
+  static_assert(SHB == 2 || (SHB == 1 && NHB == kWaves), "one score block per wave covers 64 heads");
+  constexpr int nh = SHB == 1 ? 2 : 1;  // blocks per (row, split)
   __shared__ __attribute__((aligned(16))) unsigned char ring[kSlots * kTileBytes];
   // P[head][key] bf16; the 16-byte chunk j of head h's row sits at position
   // j ^ ((h >> 2) & 3), so 16 consecutive heads read or written at one chunk
@@ -251,8 +271,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   // Blocks go round-robin over the 8 XCDs; give each XCD whole queries so the
   // splits of one query share that XCD's L2 (its query rows are read once).
   const int li = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
-  if (li >= a.row_count * ns) return;
-  const int r = li / ns, split = li % ns;
+  if (li >= a.row_count * ns * nh) return;
+  const int r = li / (ns * nh), split = (li / nh) % ns;
+  const int hoff = 64 * (li % nh);  // first head of this block
   const int t = a.row_begin + r;
   const int b = t / a.q_len;
   const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);
@@ -260,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   const int m1 = min(a.k, m0 + per_split);
   // a query that sees no key gathers nothing (its output is zero)
   const int ntiles = (m1 > m0 && pos >= 0) ? (m1 - m0 + kNT - 1) / kNT : 0;
-  const bool sh0 = NHB >= 2 * kWaves - 1 || 2 * wave < NHB;  // this wave has score heads
-  const bool sh1 = NHB >= 2 * kWaves || 2 * wave + 1 < NHB;   // ... and a second 16-head block
+  const bool sh0 = NHB >= SHB * kWaves - 1 || SHB * wave < NHB;                 // this wave has score heads
+  const bool sh1 = SHB == 2 && (NHB >= 2 * kWaves || 2 * wave + 1 < NHB);      // ... and a second 16-head block
 
   // Per-lane LDS offsets within a tile (kept as single opaque values so the
   // compiler neither splits nor re-derives them inside the tile loop): score
@@ -320,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   for (int j = 0; j < 2; ++j) {
     const bool on = j ? sh1 : sh0;
     const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + (on ? 16 * (2 * wave + j) + c : 0)) * kDQK + 8 * g;
+        static_cast<const uint16_t*>(a.q) + ((size_t)t * a.H + hoff + (on ? 16 * (SHB * wave + j) + c : 0)) * kDQK + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks)
       qf[j][ks] = on ? as_v8bf(*reinterpret_cast<const v4i*>(qrow + 32 * ks)) : as_v8bf(v4i{0, 0, 0, 0});
@@ -420,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
 #pragma unroll
       for (int j = 0; j < 4; ++j) psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[j]), ones, psum, false);
       l_part[hb] += psum;
-      *reinterpret_cast<v4i*>(pbuf + (16 * (2 * wave + hb)) * kPRow + poff) =
+      *reinterpret_cast<v4i*>(pbuf + (16 * (SHB * wave + hb)) * kPRow + poff) =
           v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
     }
   };
@@ -539,14 +560,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     if (!(hb ? sh1 : sh0)) break;
-    const int head = 16 * (2 * wave + hb) + c;
+    const int head = 16 * (SHB * wave + hb) + c;  // within the block's heads
     const float l_tot = sum_xor32(sum_xor16(l_part[hb]));
     if (g == 0) {
       hinv[head] = l_tot > 0.f ? 1.f / l_tot : 0.f;
       if (ns == 1) {
-        if (a.lse) a.lse[(size_t)t * a.H + head] = l_tot > 0.f ? (m_ref[hb] + log2f(l_tot)) * kLn2 : -INFINITY;
+        if (a.lse) a.lse[(size_t)t * a.H + hoff + head] = l_tot > 0.f ? (m_ref[hb] + log2f(l_tot)) * kLn2 : -INFINITY;
       } else {
-        float* pml = P.ml + (((size_t)r * ns + split) * a.H + head) * 2;
+        float* pml = P.ml + (((size_t)r * ns + split) * a.H + hoff + head) * 2;
         pml[0] = l_tot > 0.f ? m_ref[hb] : -INFINITY;
         pml[1] = l_tot;
       }
@@ -562,7 +583,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       if (!(hb < NHB)) break;
       const int head = 16 * hb + c;
       const float inv = hinv[head];
-      float* prow = P.o + (((size_t)r * ns + split) * a.H + head) * kDV + (kDV / kWaves) * wave + 4 * g;
+      float* prow = P.o + (((size_t)r * ns + split) * a.H + hoff + head) * kDV + (kDV / kWaves) * wave + 4 * g;
 #pragma unroll
       for (int db = 0; db < kDbW; ++db)
         *reinterpret_cast<v4f*>(prow + 16 * db) = acc_o[db][hb] * inv;
@@ -598,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
       const int hh = 64 * half + hr;
       if (hh < 16 * NHB) {
         const v4i v = *reinterpret_cast<const v4i*>(stage + hr * kStageRS + 16 * (lane & 15));
-        uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hh) * kDV;
+        uint16_t* orow = static_cast<uint16_t*>(a.out) + ((size_t)t * a.H + hoff + hh) * kDV;
         *reinterpret_cast<v4i*>(orow + (kDV / kWaves) * wave + 8 * (lane & 15)) = v;
       }
     }
@@ -611,17 +632,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
 // A wave merges one (row, head): lane l holds dims 8l..8l+7, so each split's
 // partial row is one contiguous 2 KB load (all issued before any is used).
 // Blocks for a row run on the XCD that ran its first split (the split
-// kernel gives XCD x the flat (row, split) indices [x*per_xcd,
-// (x+1)*per_xcd)), whose L2 saw the partials written.
+// kernel gives XCD x the flat (row, split, half) indices [x*per_xcd,
+// (x+1)*per_xcd), upr = ns * nh of them per row), whose L2 saw the partials
+// written.
 constexpr int kCombineMaxSplits = 8;
 constexpr int kCombineHeads = 4;  // heads (waves) per block
-__global__ __launch_bounds__(64 * kCombineHeads) void k_mla_combine(MlaArgs a, int ns, int per_xcd) {
+__global__ __launch_bounds__(64 * kCombineHeads) void k_mla_combine(MlaArgs a, int ns, int upr, int per_xcd) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
   const int hpb = a.H / kCombineHeads;  // blocks per row
-  const int r0 = (x * per_xcd + ns - 1) / ns;
-  const int r1 = min(a.row_count, ((x + 1) * per_xcd + ns - 1) / ns);
+  const int r0 = (x * per_xcd + upr - 1) / upr;
+  const int r1 = min(a.row_count, ((x + 1) * per_xcd + upr - 1) / upr);
   const int r = r0 + j / hpb;
   if (r >= r1) return;
   const int h = (j % hpb) * kCombineHeads + wave;
@@ -727,7 +749,7 @@ __global__ __launch_bounds__(256) void k_mla_f32(MlaArgs a) {
 
 size_t mla_workspace_bytes(int T, int H, int k, int is_bf16) {
   if (!is_bf16 || T <= 0) return 0;
-  const int ns = mla_splits(T, k);
+  const int ns = mla_plan(T, H, k).ns;
   if (ns == 1) return 0;
   return (size_t)T * ns * H * (2 * sizeof(float) + kDV * sizeof(float));
 }
@@ -737,26 +759,32 @@ bool mla_f32_supported(int k) { return k <= kF32MaxK; }
 hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
   if (a.row_count <= 0) return hipSuccess;
   // Splits are sized from the whole launch so partial buffers match the workspace size query.
-  const int ns = mla_splits(a.row_count, a.k);
+  const MlaPlan plan = mla_plan(a.row_count, a.H, a.k);
+  const int ns = plan.ns, upr = plan.ns * plan.nh;
   const int per = mla_per_split(a.k, ns);
-  const int total = a.row_count * ns;
+  const int total = a.row_count * upr;
   const int per_xcd = (total + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd)), block(kThreads);
-  switch (a.H / 16) {
-    case 1: hipLaunchKernelGGL(k_mla_bf16<1>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 2: hipLaunchKernelGGL(k_mla_bf16<2>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 3: hipLaunchKernelGGL(k_mla_bf16<3>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 4: hipLaunchKernelGGL(k_mla_bf16<4>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 5: hipLaunchKernelGGL(k_mla_bf16<5>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 6: hipLaunchKernelGGL(k_mla_bf16<6>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 7: hipLaunchKernelGGL(k_mla_bf16<7>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    case 8: hipLaunchKernelGGL(k_mla_bf16<8>, grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
-    default: return hipErrorInvalidValue;
+  if (plan.nh == 2) {
+    hipLaunchKernelGGL((k_mla_bf16<4, 1>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd);
+  } else {
+    switch (a.H / 16) {
+      case 1: hipLaunchKernelGGL((k_mla_bf16<1, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 2: hipLaunchKernelGGL((k_mla_bf16<2, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 3: hipLaunchKernelGGL((k_mla_bf16<3, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 4: hipLaunchKernelGGL((k_mla_bf16<4, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 5: hipLaunchKernelGGL((k_mla_bf16<5, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 6: hipLaunchKernelGGL((k_mla_bf16<6, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 7: hipLaunchKernelGGL((k_mla_bf16<7, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      case 8: hipLaunchKernelGGL((k_mla_bf16<8, 2>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   if (ns > 1) {
-    // per XCD at most ceil(per_xcd / ns) + 1 rows have their first split there
-    const int cpx = ((per_xcd + ns - 1) / ns + 1) * (a.H / kCombineHeads);
-    hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(8 * cpx)), dim3(64 * kCombineHeads), 0, stream, a, ns, per_xcd);
+    // per XCD at most ceil(per_xcd / upr) + 1 rows have their first block there
+    const int cpx = ((per_xcd + upr - 1) / upr + 1) * (a.H / kCombineHeads);
+    hipLaunchKernelGGL(k_mla_combine, dim3((unsigned)(8 * cpx)), dim3(64 * kCombineHeads), 0, stream, a, ns, upr,
+                       per_xcd);
   }
   return hipGetLastError();
 }
