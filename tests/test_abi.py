@@ -279,3 +279,20 @@ def test_forward_noalloc_rejects_before_touching_the_device():
     assert call(ctypes.byref(big)) == 3
     assert call(None) == 1
     assert call(ctypes.byref(_geom(B=2, q_len=1, S=4096)), H=0) == 1
+
+
+def test_sparse_mla_workspace_follows_the_split_plan():
+    """The bf16 attention's workspace is its fp32 split partials,
+    rows x splits x H x (512 + 2) floats.  With 128 heads and too few rows
+    for one split each, a (row, split) runs as two 64-head blocks, so the
+    256-block launch needs half the splits: 32 rows x top-2048 take 4 splits
+    (not 8), 64 rows 2, 96 rows at k = 1024 one (no partials); other head
+    counts keep one block per (row, split) (32 rows, 64 heads: 8 splits)."""
+    lib = lcl.load()
+    per = lambda T, ns, H: T * ns * H * (512 + 2) * 4
+    assert lib.dsa_sparse_mla_workspace_size(16, 2, 128, 2048, 1) == per(32, 4, 128)
+    assert lib.dsa_sparse_mla_workspace_size(64, 1, 128, 2048, 1) == per(64, 2, 128)
+    assert lib.dsa_sparse_mla_workspace_size(48, 2, 128, 1024, 1) == 0
+    assert lib.dsa_sparse_mla_workspace_size(16, 2, 64, 2048, 1) == per(32, 8, 64)
+    assert lib.dsa_sparse_mla_workspace_size(4096, 1, 128, 2048, 1) == 0        # prefill: one split per row
+    assert lib.dsa_sparse_mla_workspace_size(16, 2, 128, 2048, 0) == 0          # fp32 path: no partials

@@ -103,6 +103,9 @@ MLA_CASES = [
     # name, B, q_len, seq_lens, S_max, k, H, bf16
     ("decode_bf16", 3, 2, [5000, 3000, 2], 5000, 512, 128, True),
     ("decode_bf16_h32", 2, 1, [4000, 100], 4000, 300, 32, True),
+    # 96 rows, k = 1024: one split per row, each row's 128 heads as two
+    # 64-head blocks that write the output directly (no partials)
+    ("decode_bf16_halves_1split", 48, 2, [2500, 1800, 1100, 2500, 2047, 1025] * 8, 2500, 1024, 128, True),
     ("prefill_bf16", 1, 96, [1000], 1000, 256, 64, True),
     ("tiny_f32", 1, 64, [200], 200, 64, 16, False),
 ]
