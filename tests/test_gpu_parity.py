@@ -106,6 +106,8 @@ MLA_CASES = [
     # 96 rows, k = 1024: one split per row, each row's 128 heads as two
     # 64-head blocks that write the output directly (no partials)
     ("decode_bf16_halves_1split", 48, 2, [2500, 1800, 1100, 2500, 2047, 1025] * 8, 2500, 1024, 128, True),
+    # one query, 128 heads, top-2048: 8 splits x two 64-head blocks (16 blocks)
+    ("decode_bf16_one_query", 1, 1, [3000], 3000, 2048, 128, True),
     ("prefill_bf16", 1, 96, [1000], 1000, 256, 64, True),
     ("tiny_f32", 1, 64, [200], 200, 64, 16, False),
 ]
