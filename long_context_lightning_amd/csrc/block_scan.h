@@ -52,4 +52,25 @@ __device__ __forceinline__ uint32_t block_exclusive_sum(uint32_t v, uint32_t* sm
   return res;
 }
 
+// The same prefix sum with a single barrier: every wave reads all the wave
+// totals.  `sm` needs NT/64 words; there is no trailing barrier, so the
+// caller must not write sm[0 .. NT/64) again before a later barrier.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_sum_once(uint32_t v, uint32_t* sm, uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_sum(v);
+  if (lane == 63) sm[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = sm[w];
+    base += (w < wave) ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return base + inc - v;
+}
+
 }  // namespace dsa

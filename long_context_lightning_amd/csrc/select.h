@@ -83,7 +83,8 @@ __device__ void radix_select_desc(ForEach&& for_each, uint32_t& prefix, int rem_
 // folds them into `bitmap`, and writes all set positions in ascending order
 // to out[0..limit).  Thread t owns the contiguous words
 // [t*per, (t+1)*per), per a multiple of 4.  Returns the number of set
-// positions.  `sm` needs NT/64 + 4 words.  Block-wide.
+// positions.  `sm` needs NT/64 + 4 words, and other threads may still read
+// it on return: a barrier must come before it is written again.  Block-wide.
 template <int NT>
 __device__ uint32_t bitmap_select_emit(uint32_t* bitmap, const uint32_t* tbits, int n, uint32_t want, int32_t* out,
                                        uint32_t limit, uint32_t* sm) {
@@ -136,7 +137,7 @@ __device__ uint32_t bitmap_select_emit(uint32_t* bitmap, const uint32_t* tbits, 
     b4[gi] = b;
   }
   uint32_t total;
-  uint32_t off = block_exclusive_sum<NT>(cnt, sm, &total);
+  uint32_t off = block_exclusive_sum_once<NT>(cnt, sm, &total);  // sm is not written again here
   // 3. positions in ascending order
   for (int gi = g0; gi < g1; ++gi) {
     const v4i b = b4[gi];
@@ -157,7 +158,9 @@ __device__ uint32_t bitmap_select_emit(uint32_t* bitmap, const uint32_t* tbits, 
 // Writes the set positions of `bitmap` (n positions, zero up to the next
 // multiple of 4 words) in ascending order to out[0..limit).  Thread t owns
 // the contiguous 16-byte groups [t*per, (t+1)*per).  Returns the number of
-// set positions.  `sm` needs NT/64 + 4 words.  Block-wide.
+// set positions.  `sm` needs NT/64 + 4 words, and other threads may still
+// read it on return: a barrier must come before it is written again.
+// Block-wide.
 template <int NT>
 __device__ uint32_t bitmap_emit(const uint32_t* bitmap, int n, int32_t* out, uint32_t limit, uint32_t* sm) {
   const int W4 = (((n + 31) >> 5) + 3) >> 2;  // 16-byte groups
@@ -170,7 +173,7 @@ __device__ uint32_t bitmap_emit(const uint32_t* bitmap, int n, int32_t* out, uin
     cnt += __popc((uint32_t)b[0]) + __popc((uint32_t)b[1]) + __popc((uint32_t)b[2]) + __popc((uint32_t)b[3]);
   }
   uint32_t total;
-  uint32_t off = block_exclusive_sum<NT>(cnt, sm, &total);
+  uint32_t off = block_exclusive_sum_once<NT>(cnt, sm, &total);  // sm is not written again here
   for (int gi = g0; gi < g1; ++gi) {
     const v4i b = b4[gi];
 #pragma unroll
