@@ -133,6 +133,44 @@ def test_topk_largest_rows(dsa_gpu):
             assert np.array_equal(idx[r], want), f"k={k} row {r}"
 
 
+def test_topk_threshold_bin_regimes(dsa_gpu):
+    """128K rows (several blocks per row), k = 2048, built so the threshold
+    bin's candidates take each branch of the final selection: few
+    candidates (at most 4096: four register slots per thread), a crowded
+    bin (4096 < candidates <= 2k + 4096: twelve slots) whose next 10 bits are
+    resolved by the second histogram with ties at the k-th score, a bin
+    whose next 10 bits hold exactly the remaining count (taken whole), and an
+    overflowing bin (the selection falls back to the score row); exact
+    against the oracle's rule."""
+    _say("[topk] 128K rows: threshold-bin regimes of the final selection")
+    rng = np.random.default_rng(21)
+    S, k = 131072, 2048
+    B = 4
+    scores = rng.uniform(-1.0, 0.5, (B, S)).astype(np.float32)
+    # row 0: a plain spread, few candidates in the threshold bin
+    scores[0] = rng.standard_normal(S).astype(np.float32)
+    # row 1: 1500 clear winners, then 5000 scores inside one 12-bit bin
+    # [1, 1.125) drawn from 640 values (ties at the k-th score)
+    p1 = rng.permutation(S)
+    scores[1, p1[:1500]] = rng.uniform(100.0, 200.0, 1500)
+    scores[1, p1[1500:6500]] = (1.0 + rng.integers(0, 640, 5000) / 8192.0).astype(np.float32)
+    # row 2: 2000 winners, then a bin whose top 10-bit digit holds exactly 48 scores
+    p2 = rng.permutation(S)
+    scores[2, p2[:2000]] = rng.uniform(100.0, 200.0, 2000)
+    scores[2, p2[2000:2048]] = np.float32(1.0 + 1023.0 / 8192.0)       # the highest digit of [1, 1.125)
+    scores[2, p2[2048:5000]] = (1.0 + rng.integers(0, 1000, 2952) / 8192.0).astype(np.float32)
+    # row 3: 9000 scores in one bin above everything else (more than 2k + 4096)
+    p3 = rng.permutation(S)
+    scores[3, p3[:9000]] = (1.0 + rng.integers(0, 1024, 9000) / 8192.0).astype(np.float32)
+    seq = np.full(B, S, np.int32)
+    d_seq = torch.from_numpy(seq).cuda()
+    g = dsa_gpu.make_geom(B, 1, S, d_seq)
+    idx = dsa_gpu.topk(g, torch.from_numpy(scores).cuda(), k).cpu().numpy()
+    for r in range(B):
+        want, _ = topk_select(scores[r].astype(np.float64), S - 1, k)
+        assert np.array_equal(idx[r], want), f"row {r}"
+
+
 @pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
 def test_sparse_mla(dsa_gpu, case):
     name, B, q_len, seq, S, k, H, bf16 = case
