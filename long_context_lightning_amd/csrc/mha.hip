@@ -232,8 +232,16 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, c = lane & 15;
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int qt = (int)gridDim.x - 1 - (int)blockIdx.x;  // longest query tiles first
+  // Work items go longest query tile first, then (sequence, head).  Blocks
+  // are dealt round-robin over the 8 XCDs by their linear index, so taking
+  // items in that order gives every XCD an equal share of every query tile
+  // (the query tile as the fastest block index would hand all blocks of one
+  // tile length to one XCD and leave the short-tile XCDs idle most of the
+  // launch).
+  const int nbh = (int)(gridDim.y * gridDim.z);
+  const int item = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int qt = (int)gridDim.x - 1 - item / nbh;
+  const int h = (item % nbh) % (int)gridDim.y, b = (item % nbh) / (int)gridDim.y;
   const int L = clamped_len(a.seq_lens, b, a.S_max);
   const int i0 = qt * kAQ;                               // first query index within the sequence
   const int i1 = min(i0 + kAQ, a.q_len);

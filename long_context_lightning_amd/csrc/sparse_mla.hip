@@ -40,6 +40,7 @@ namespace dsa {
 namespace {
 
 constexpr int kNT = 32;                          // keys per tile
+constexpr int kRowChunk = 16;                    // consecutive rows per XCD turn (one block per row)
 constexpr int kMainRS = 1056;                    // LDS stride of a row's dims 0..511 (1024 bytes + 32 pad)
 constexpr int kMainBytes = kNT * kMainRS;        // 33792
 constexpr int kRopeRS = 128;                     // dims 512..575 of a row: 8 pieces, XOR-swizzled
@@ -268,10 +269,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
-  // Blocks go round-robin over the 8 XCDs; give each XCD whole queries so the
-  // splits of one query share that XCD's L2 (its query rows are read once).
-  const int li = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
-  if (li >= a.row_count * ns * nh) return;
+  // Blocks go round-robin over the 8 XCDs.  With several blocks per row, an
+  // XCD takes a contiguous range of whole rows, so the splits and halves of
+  // one query share that XCD's L2 (its query rows are read once).  With one
+  // block per row, the rows go to the XCDs in chunks of kRowChunk, dealt
+  // round-robin and last rows first: every XCD gets an equal share of a
+  // causal prefill's short early rows, which otherwise all fall on the first
+  // XCD, and the long rows start first.
+  int li;
+  if (ns * nh == 1) {
+    const int x = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
+    li = a.row_count - 1 - (((j / kRowChunk) * 8 + x) * kRowChunk + j % kRowChunk);
+    if (li < 0) return;
+  } else {
+    li = ((int)blockIdx.x % 8) * per_xcd + (int)blockIdx.x / 8;
+    if (li >= a.row_count * ns * nh) return;
+  }
   const int r = li / (ns * nh), split = (li / nh) % ns;
   const int hoff = 64 * (li % nh);  // first head of this block
   const int t = a.row_begin + r;
@@ -763,7 +776,8 @@ hipError_t launch_mla_bf16(const MlaArgs& a, hipStream_t stream) {
   const int ns = plan.ns, upr = plan.ns * plan.nh;
   const int per = mla_per_split(a.k, ns);
   const int total = a.row_count * upr;
-  const int per_xcd = (total + 7) / 8;
+  // blocks per XCD: whole rows (several blocks per row), or whole row chunks
+  const int per_xcd = upr == 1 ? ((total + kRowChunk - 1) / kRowChunk + 7) / 8 * kRowChunk : (total + 7) / 8;
   const dim3 grid((unsigned)(8 * per_xcd)), block(kThreads);
   if (plan.nh == 2) {
     hipLaunchKernelGGL((k_mla_bf16<4, 1>), grid, block, 0, stream, a, a.idx, ns, per, per_xcd);
