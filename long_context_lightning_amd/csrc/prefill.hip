@@ -466,10 +466,14 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   const int g = lane >> 4, c = lane & 15;
   const unsigned long long lt = (1ull << lane) - 1ull;
 
-  // Longest rows first: block j -> query block (nqb-1-j/B) of sequence j%B.
+  // Longest rows first: block j -> query block nqb-1-j/B.  The B blocks of a
+  // query block take the sequences in an order rotated once per round of 8
+  // blocks: the XCDs take blocks round-robin, so with several sequences every
+  // XCD sees all of them instead of a fixed subset.
   const int nqb = (a.q_len + kRows - 1) / kRows;
-  const int b = (int)blockIdx.x % a.B;
-  const int qb = nqb - 1 - (int)blockIdx.x / a.B;
+  const int grp = (int)blockIdx.x / a.B;
+  const int b = ((int)blockIdx.x % a.B + grp / max(1, 8 / a.B)) % a.B;
+  const int qb = nqb - 1 - grp;
   const int L = clamped_len(a.seq_lens, b, a.S_max);
   const int i0 = qb * kRows;                       // first query index in the sequence
   const int nrows = min(kRows, a.q_len - i0);

@@ -195,6 +195,7 @@ FWD_CASES = [
     ("fwd_decode_ties", 2, 2, [7000, 7000], 7000, 512, 16, "pool"),
     ("fwd_prefill_stream", 1, 1500, [1500], 1500, 256, 16, "normal"),
     ("fwd_prefill_stream_b2", 2, 200, [2600, 300], 2600, 128, 16, "normal"),
+    ("fwd_prefill_stream_b5", 5, 96, [700, 300, 1200, 96, 2000], 2000, 256, 16, "normal"),  # rotated sequence order
     ("fwd_keep_all", 2, 70, [300, 100], 300, 512, 16, "normal"),   # S_max <= topk: indexer bypassed
 ]
 
