@@ -19,7 +19,9 @@
 //   positions, so each copy instruction feeds 8 MFMAs.  64-deep K chunks of
 //   both operands go global -> LDS by DMA (double buffered), 16-byte pieces
 //   XOR-swizzled so the 16 rows one fragment read covers fall on distinct
-//   banks.  Output head-major: k_nope[b][h][s][128], v[b][h][s][128] bf16.
+//   banks.  Output head-major: k_nope[b][h][s][128], v[b][h][s][128] bf16,
+//   staged through LDS so a block writes its two contiguous 64 KB regions in
+//   whole 1 KB pieces.
 //
 // k_mha_attn: one block = one head x 256 consecutive queries of one
 //   sequence, 8 waves (two per SIMD) of 32 queries.  Keys stream in 64-key
@@ -83,6 +85,8 @@ constexpr int kGStage = kGW + kGX;
 constexpr int kGSteps = kDL / kGK;       // 8
 constexpr int kGWaves = 8;
 constexpr int kGDma = kGStage / 1024 / kGWaves;  // DMA instructions per wave per stage (8)
+constexpr int kGORow = 2 * kGN;          // bytes of one output position row in LDS (512)
+static_assert(kGT * kGORow <= 2 * kGStage, "the staged output fits in the two stages");
 
 // Stage kc of the block's operands: the head's 256 W rows (output columns)
 // then 256 latent rows (positions), 128 bytes per row; lane l of instruction
@@ -156,20 +160,35 @@ __global__ __launch_bounds__(kGWaves * 64, 1) void k_mha_decompress(MhaArgs a) {
     }
     lds_barrier();  // the next step refills this stage
   }
-  // D[column 4g + i'][position c] of block (i, j): four consecutive columns of
-  // one position per lane -> one 8-byte store; columns 0..127 are k_nope,
-  // 128..255 are v.
-  uint16_t* dst = static_cast<uint16_t*>(wn < 2 ? a.knope_ws : a.v_ws) + ((size_t)b * a.H + h) * a.S_max * kDVh;
-  const int col0 = 64 * (wn & 1);
+  // The output goes out through LDS (both stages are free after the last
+  // step's barrier): position p's row of 256 bf16 columns (k_nope | v, 512
+  // bytes) has its 16-byte chunk q at q ^ (p & 31), so the 16 positions one
+  // register write covers fall on distinct banks.  The block's k_nope and v
+  // outputs are each one contiguous region of the head-major workspace, so
+  // the copy-out is whole 1 KB pieces, 16 bytes per lane.
+  // acc[i][j][e]: column 64 wn + 16 i + 4 g + e of position 128 wsb + 16 j + c.
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const int s = s0 + 128 * wsb + 16 * j + c;
-    if (s >= L) continue;
+    const int p = 128 * wsb + 16 * j + c;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint2 pk = pack4_bf16(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-      *reinterpret_cast<uint2*>(dst + (size_t)s * kDVh + col0 + 16 * i + 4 * g) = pk;
+      const int byte = 128 * wn + 32 * i + 8 * g;  // in the position's 512-byte row
+      *reinterpret_cast<uint2*>(lds + p * kGORow + 16 * ((byte >> 4) ^ (p & 31)) + (byte & 15)) =
+          pack4_bf16(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
+  }
+  __syncthreads();
+  const int nvalid = min(kGT, L - s0);  // positions past the sequence are not written
+  const size_t obase = (((size_t)b * a.H + h) * a.S_max + s0) * kDVh;
+  uint16_t* const kdst = static_cast<uint16_t*>(a.knope_ws) + obase;
+  uint16_t* const vdst = static_cast<uint16_t*>(a.v_ws) + obase;
+#pragma unroll 4
+  for (int q = (int)threadIdx.x; q < 2 * kGT * 16; q += kGWaves * 64) {
+    const int part = q / (kGT * 16), qq = q % (kGT * 16);  // part 0: k_nope, 1: v
+    const int p = qq >> 4, cc = qq & 15;                  // position, 16-byte chunk of its 256-byte row
+    if (p >= nvalid) continue;
+    const v4i val = *reinterpret_cast<const v4i*>(lds + p * kGORow + 16 * ((cc + 16 * part) ^ (p & 31)));
+    *reinterpret_cast<v4i*>((part ? vdst : kdst) + (size_t)p * kDVh + 8 * cc) = val;
   }
 }
 
