@@ -429,21 +429,38 @@ __global__ __launch_bounds__(kAW * 64, 1) void k_mha_attn(MhaArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // out[t, h, dims 16 db + 4g .. +3] for query c of block qb; lse by the g = 0 lanes
+  // Output rows out[t, h, :] (256 bytes each, consecutive queries H rows
+  // apart) go out through the ring slot after the last tile's: every wave is
+  // past the last tile barrier and no copy is in flight, so that slot is
+  // free.  Each wave stages one 16-query block at a time in its own 4 KB
+  // (query c's row, 16-byte chunk j at j ^ c, so a register write covers
+  // 16 banks), then writes whole rows, 16 bytes per lane; the stage is
+  // private to the wave, whose LDS accesses complete in order.  lse by the
+  // g = 0 lanes.  Lane (g, c) holds dims 16 db + 4g .. +3 of query c.
+  unsigned char* const ost = ring + (ntiles % kASlots) * kAStage + wave * (16 * 2 * kDVh);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qi = wi0 + 16 * qb + c;
-    if (qi >= i1) continue;
     const float l = sum_xor32(sum_xor16(l_run[qb]));
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const size_t t = (size_t)b * a.q_len + qi;
-    uint16_t* orow = static_cast<uint16_t*>(a.out) + (t * a.H + h) * kDVh;
 #pragma unroll
     for (int db = 0; db < kDVh / 16; ++db) {
       const v4f o = acc[db][qb];
-      *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g) = pack4_bf16(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+      const int byte = 32 * db + 8 * g;  // in the query's 256-byte row
+      *reinterpret_cast<uint2*>(ost + c * (2 * kDVh) + 16 * ((byte >> 4) ^ c) + (byte & 15)) =
+          pack4_bf16(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
     }
-    if (a.lse && g == 0) a.lse[t * a.H + h] = l > 0.f ? (m_ref[qb] + log2f(l)) * kLn2 : -INFINITY;
+    const int qi = wi0 + 16 * qb + c;
+    if (qi < i1 && a.lse && g == 0)
+      a.lse[((size_t)b * a.q_len + qi) * a.H + h] = l > 0.f ? (m_ref[qb] + log2f(l)) * kLn2 : -INFINITY;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int row = 4 * it + (lane >> 4), j = lane & 15;
+      const int qr = wi0 + 16 * qb + row;
+      if (qr < i1) {
+        const v4i v = *reinterpret_cast<const v4i*>(ost + row * (2 * kDVh) + 16 * (j ^ row));
+        *reinterpret_cast<v4i*>(static_cast<uint16_t*>(a.out) + (((size_t)b * a.q_len + qr) * a.H + h) * kDVh + 8 * j) = v;
+      }
+    }
   }
 }
 
