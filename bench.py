@@ -733,12 +733,14 @@ def _oracle_rows(oracle, np, wl, rows, qi, w, ki, ks, qm, kv):
 
 def cpu_baseline_configs(np, budget_s):
     """The float64 oracle on the other fp8 configurations, each on a bounded
-    sample (about budget_s / 3 seconds each), on the host cores:
-      decode32k   whole sequences (one query each), queries/s;
-      prefill8k   the 32 planted rows plus 32 seeded uniformly random rows:
-                  rows/s on the sample, and the full 8192-row run
-                  extrapolated from the random rows (mean time per row x L);
-      prefill64k  seeded uniformly random rows, same report.
+    sample, on the host cores:
+      decode32k   whole sequences (one query each) until about budget_s / 3
+                  seconds have passed, queries/s;
+      prefill8k   the 32 planted rows plus 32 seeded uniformly random rows
+                  (a fixed sample of about a second): rows/s on the sample,
+                  and the full 8192-row run extrapolated from the random rows
+                  (mean time per row x L);
+      prefill64k  12 seeded uniformly random rows, same report.
     Inputs follow the same recipe (synth); only the sampled rows' queries
     are drawn."""
     import oracle
