@@ -423,26 +423,33 @@ __device__ __forceinline__ void emit_pool_rows(const TopkArgs& a, int r, const i
 // The final selection of a row whose candidates fit the list (total of
 // them, at most NP per thread): the gather's histogram of bin b* gives the
 // next 10 bits of tau, select_tail the rest.
+// Wave 0's lane l reads the 16 contiguous second-histogram digits
+// [kBins2 - 16 (l + 1), kBins2 - 16 l): c[j] is digit d0 + j.
+__device__ __forceinline__ void load_hist2(const uint32_t* hist2, uint32_t (&c)[kBins2 / 64]) {
+  constexpr int kPer = kBins2 / 64;
+  const int d0 = kBins2 - kPer * ((int)threadIdx.x + 1);
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const v4i v = *reinterpret_cast<const v4i*>(&hist2[d0 + 4 * q]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[4 * q + e] = (uint32_t)v[e];
+  }
+}
 template <int NP>
-__device__ void final_from_candidates(const TopkArgs& a, int n, int32_t* out, const RowWs& w, uint32_t bstar,
-                                      uint32_t above, uint32_t total, const SelLds& L) {
+__device__ void final_from_candidates(const TopkArgs& a, int n, int32_t* out, uint32_t bstar, uint32_t above,
+                                      uint32_t total, const uint32_t (&c)[kBins2 / 64], const RowWs& w,
+                                      const SelLds& L) {
   uint32_t ck[NP], cp[NP];
   load_candidates<NP>(w.ekey, w.eidx, total, ck, cp);
   clear_bitmaps(L, (((n + 31) >> 5) + 3) & ~3);
   const uint32_t want = (uint32_t)a.k - above;
-  // The next 10 bits of tau come from the gather's histogram of bin b*:
-  // lane l holds the 16 contiguous digits [d0, d0 + 16) and the lanes walk
-  // them from the top, as in the digit scan of select_tail.
+  // The next 10 bits of tau come from the gather's histogram of bin b*
+  // (wave 0's c, from load_hist2): lane l holds the 16 contiguous digits
+  // [d0, d0 + 16) and the lanes walk them from the top, as in the digit scan
+  // of select_tail.
   if (threadIdx.x < 64) {
     constexpr int kPer = kBins2 / 64;
     const int d0 = kBins2 - kPer * ((int)threadIdx.x + 1);
-    uint32_t c[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer / 4; ++q) {
-      const v4i v = *reinterpret_cast<const v4i*>(&w.hist2[d0 + 4 * q]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c[4 * q + e] = (uint32_t)v[e];
-    }
     uint32_t tot = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) tot += c[j];
@@ -475,6 +482,10 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
     for (int j = threadIdx.x; j < a.k; j += kFinThreads) out[j] = (j < n) ? j : -1;
   } else {
     const RowWs w = row_ws(a.ws, r, a.k);
+    // Wave 0 reads the second histogram before the counts that size the
+    // candidate loads, so its digit scan overlaps those loads.
+    uint32_t h2[kBins2 / 64];
+    if (threadIdx.x < 64) load_hist2(w.hist2, h2);
     const uint32_t bstar = w.meta[1], above = w.meta[2], inbin = w.meta[3];
     const SelLds L = sel_lds(dyn, a.S_max);
     const uint32_t total = above + inbin;
@@ -482,9 +493,9 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
       select_direct(a, r, n, out, L);
     } else {
       if (total <= (uint32_t)(kCPerSmall * kFinThreads))
-        final_from_candidates<kCPerSmall>(a, n, out, w, bstar, above, total, L);
+        final_from_candidates<kCPerSmall>(a, n, out, bstar, above, total, h2, w, L);
       else
-        final_from_candidates<kCPer>(a, n, out, w, bstar, above, total, L);
+        final_from_candidates<kCPer>(a, n, out, bstar, above, total, h2, w, L);
     }
   }
   emit_pool_rows(a, r, out);
