@@ -182,6 +182,25 @@ DSA_API dsa_status dsa_forward(const dsa_geom* geom, int32_t H, int32_t topk, fl
 DSA_API size_t dsa_forward_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H,
                                   int32_t topk, dsa_dtype index_dtype, dsa_dtype mla_dtype);
 
+/* The indexer and the top-k of dsa_forward without the attention: the
+ * Indexer's forward, which returns topk_indices ("详解DSA", Indexer code
+ * block: Eq.(1) scores, then topk(min(index_topk, end_pos))).  Arguments as
+ * in dsa_forward; idx_out [T, topk] int32 (required, device memory)
+ * receives exactly the selection dsa_forward computes for the same inputs:
+ * ascending positions, -1 padded.  Long prefills (q_len >= 64 with fp8
+ * inputs) stream the scores as dsa_forward does; other shapes score into the
+ * workspace chunk by chunk; with S_max <= topk every position is selected
+ * and the indexer does not run (its inputs are still validated).  Errors as
+ * dsa_forward's (DSA_ERR_INVALID_ARG for a NULL idx_out).
+ * ws >= dsa_indexer_topk_workspace_size(...) bytes (0 when S_max <= topk). */
+DSA_API dsa_status dsa_indexer_topk(const dsa_geom* geom, int32_t topk,
+                            const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
+                            const void* index_w, dsa_dtype index_w_dtype,
+                            const void* index_k, const float* index_k_scale,
+                            int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
+DSA_API size_t dsa_indexer_topk_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t topk,
+                                       dsa_dtype index_dtype);
+
 /* Per-block fp8 quantisation of indexer inputs (the act_quant step of the
  * "详解DSA" Indexer code block, applied there to q and to k before the key
  * cache stores k; the "DSA计算流" section of that page keeps each key's scale
@@ -349,7 +368,8 @@ DSA_API size_t dsa_indexer_kl_workspace_size(int32_t B, int32_t q_len, int32_t S
  * dtype combination the call supports (the maximum of its own
  * *_workspace_size query over them), so a caller can size one buffer before
  * it knows the dtypes.  k is the top-k / selection width (dsa_topk's k,
- * dsa_sparse_mla's k, dsa_forward's topk, dsa_indexer_kl's k with 0 = every
+ * dsa_sparse_mla's k, dsa_forward's and dsa_indexer_topk's topk,
+ * dsa_indexer_kl's k with 0 = every
  * visible position); H the MLA heads.  For DSA_CALL_TOPK the rows are all
  * B*q_len rows.  The forward sizes assume idx_out != NULL (with NULL add
  * B*q_len*k*4 bytes rounded up to 256).  Returns 0 for calls that need no
@@ -361,7 +381,8 @@ typedef enum {
   DSA_CALL_SPARSE_MLA_PAGED = 3,
   DSA_CALL_FORWARD_PAGED = 4,
   DSA_CALL_MHA_PREFILL = 5,
-  DSA_CALL_INDEXER_KL = 6
+  DSA_CALL_INDEXER_KL = 6,
+  DSA_CALL_INDEXER_TOPK = 7
 } dsa_call;
 DSA_API size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, int32_t k,
                                   int which_call);

@@ -59,6 +59,8 @@ def load(path=None):
         "dsa_forward": (i32, [gp, i32, i32, f32, vp, i32, vp, vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, sz,
                               vp]),
         "dsa_forward_workspace_size": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+        "dsa_indexer_topk": (i32, [gp, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "dsa_indexer_topk_workspace_size": (sz, [i32, i32, i32, i32, i32]),
         "dsa_indexer_quantize": (i32, [vp, i32, i64, vp, vp, vp]),
         "dsa_indexer_cache_append": (i32, [gp, vp, i32, vp, vp, vp]),
         "dsa_indexer_scores_paged": (i32, [gp, pp, vp, i32, vp, vp, i32, vp, i32, vp, i32, i32, vp, i64, vp]),
@@ -87,6 +89,7 @@ def load(path=None):
 
 ABI_FUNCTIONS = ("dsa_indexer_scores", "dsa_topk", "dsa_topk_workspace_size", "dsa_sparse_mla",
                  "dsa_sparse_mla_workspace_size", "dsa_forward", "dsa_forward_workspace_size",
+                 "dsa_indexer_topk", "dsa_indexer_topk_workspace_size",
                  "dsa_indexer_quantize", "dsa_indexer_cache_append", "dsa_indexer_scores_paged",
                  "dsa_sparse_mla_paged", "dsa_sparse_mla_paged_workspace_size", "dsa_forward_paged",
                  "dsa_forward_paged_workspace_size", "dsa_indexer_cache_append_paged", "dsa_mha_prefill",
@@ -97,7 +100,7 @@ NOALLOC_SCRATCH_BYTES = 96 << 20   # DSA_NOALLOC_SCRATCH_BYTES
 
 # which_call values of dsa_workspace_size
 CALL_TOPK, CALL_SPARSE_MLA, CALL_FORWARD, CALL_SPARSE_MLA_PAGED, CALL_FORWARD_PAGED, CALL_MHA_PREFILL, \
-    CALL_INDEXER_KL = range(7)
+    CALL_INDEXER_KL, CALL_INDEXER_TOPK = range(8)
 
 
 def _ptr(t):
@@ -274,6 +277,34 @@ def sparse_mla(geom, q, kv, idx, sm_scale, out=None, lse=None, ws=None, want_lse
 
 def forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype):
     return int(load().dsa_forward_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype))
+
+
+def indexer_topk_workspace_size(B, q_len, S_max, topk_k, index_dtype):
+    return int(load().dsa_indexer_topk_workspace_size(B, q_len, S_max, topk_k, index_dtype))
+
+
+def indexer_topk(geom, topk_k, index_q, index_w, index_k, index_k_scale=None, index_q_scale=None, idx=None, ws=None,
+                 stream=None):
+    """dsa_indexer_topk: the indexer and the top-k of dsa_forward, without the
+    attention.  Returns idx [T, topk_k] int32 (ascending, -1 padded)."""
+    lib = load()
+    T = geom.B * geom.q_len
+    dev = index_q.device
+    if idx is None:
+        idx = torch.empty((T, topk_k), dtype=torch.int32, device=dev)
+    idt = _index_dtype(index_q)
+    need = indexer_topk_workspace_size(geom.B, geom.q_len, geom.S_max, topk_k, idt)
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    for name, t in (("index_q", index_q), ("index_w", index_w), ("index_k", index_k), ("idx", idx)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous device tensor")
+    _need(tuple(index_q.shape) == (T, 64, 128) and tuple(index_k.shape) == _cache_shape(geom, None, (128,)),
+          "indexer shapes mismatch")
+    _need(tuple(idx.shape) == (T, topk_k) and idx.dtype == torch.int32, "idx must be [T, topk] int32")
+    _check(lib.dsa_indexer_topk(ctypes.byref(geom), topk_k, _ptr(index_q), idt, _ptr(index_q_scale), _ptr(index_w),
+                                _w_dtype(index_w), _ptr(index_k), _ptr(index_k_scale), _ptr(idx), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "dsa_indexer_topk")
+    return idx
 
 
 def forward_paged_workspace_size(B, q_len, S_max, H, topk_k, index_dtype, mla_dtype):

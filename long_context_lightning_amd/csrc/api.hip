@@ -171,6 +171,7 @@ MlaArgs make_mla_args(const dsa_geom* g, int32_t H, int32_t k, float sm_scale, c
   a.row_begin = 0;
   a.row_count = (int)rows_of(g);
   a.flat = 0;
+  a.sel_prefix = 0;
   return a;
 }
 
@@ -238,10 +239,13 @@ dsa_status indexer_scores_impl(const dsa_geom* geom, const dsa_pages* pages, con
 
 // The attention over translated pool rows (paged) or positions (contiguous).
 // rows_ready: the top-k launch has already written the pool rows.
+// sel_prefix: idx is the forward's own selection (valid entries first).
 hipError_t mla_launches(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t k, float sm_scale,
                         const void* q, dsa_dtype dtype, const void* kv, const int32_t* idx, void* out, float* lse,
-                        void* mla_ws, int32_t* rows, hipStream_t stream, bool rows_ready = false) {
+                        void* mla_ws, int32_t* rows, hipStream_t stream, bool rows_ready = false,
+                        bool sel_prefix = false) {
   MlaArgs a = make_mla_args(geom, H, k, sm_scale, q, kv, idx, out, lse, mla_ws);
+  a.sel_prefix = sel_prefix ? 1 : 0;
   if (pages) {
     const hipError_t e = rows_ready ? hipSuccess
                                     : launch_page_rows(idx, rows, (int)rows_of(geom), k, geom->q_len, geom->S_max,
@@ -267,6 +271,75 @@ dsa_status sparse_mla_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t
   return hip_status(mla_launches(geom, pages, H, k, sm_scale, q, dtype, kv, idx, out, lse, ws, rows, stream));
 }
 
+// The selection of dsa_forward (stages a1 and a2) into idx_out: the keep-all
+// rows when S_max <= topk, the streamed indexer + top-k of long fp8
+// prefills, else the indexer's score rows chunk by chunk into the workspace
+// and the top-k over them.  With pages, the top-k of the chunked path also
+// writes the selection as pool rows into rows (when rows is not null).
+// The workspace layout is plan p's, below p.mla_off.
+hipError_t select_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t topk, const void* index_q,
+                       dsa_dtype index_dtype, const float* index_q_scale, const void* index_w,
+                       dsa_dtype index_w_dtype, const void* index_k, const float* index_k_scale, int32_t* idx_out,
+                       char* wsb, const ForwardPlan& p, int32_t* rows, hipStream_t stream) {
+  const int T = (int)rows_of(geom);
+  if (geom->S_max <= topk) {
+    // "详解DSA", DSA计算流: a sequence no longer than top-k keeps every
+    // position, so the indexer's work is skipped; the selection is 0 .. pos.
+    TopkArgs ta{};
+    ta.B = geom->B;
+    ta.q_len = geom->q_len;
+    ta.S_max = geom->S_max;
+    ta.seq_lens = geom->seq_lens;
+    ta.row_begin = 0;
+    ta.row_count = T;
+    ta.k = topk;
+    ta.idx = idx_out;
+    return launch_select_all(ta, stream);
+  }
+  IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
+  ia.pages = page_map(pages);
+  if (p.streaming) {
+    ia.row_begin = 0;
+    ia.row_count = T;
+    return launch_indexer_topk_prefill(ia, topk, idx_out, wsb, stream);
+  }
+  hipError_t e = hipSuccess;
+  float* scores = reinterpret_cast<float*>(wsb + p.scores_off);
+  const bool fp8 = index_dtype == DSA_FP8_E4M3FN;
+  for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
+    const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
+    TopkArgs ta{};
+    ta.B = geom->B;
+    ta.q_len = geom->q_len;
+    ta.S_max = geom->S_max;
+    ta.seq_lens = geom->seq_lens;
+    ta.scores = scores;
+    ta.ld = geom->S_max;
+    ta.row_begin = r0;
+    ta.row_count = rc;
+    ta.k = topk;
+    ta.idx = idx_out + (long long)r0 * topk;
+    ta.ws = wsb + p.topk_off;
+    ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
+    if (pages && rows) {  // the top-k also writes the selection as pool rows
+      ta.rows = rows + (long long)r0 * topk;
+      ta.pages = page_map(pages);
+    }
+    ia.row_begin = r0;
+    ia.row_count = rc;
+    ia.scores = scores;
+    ia.ld = geom->S_max;
+    if (!topk_row_fused(geom->S_max, topk)) {  // the multi-launch top-k counts into cleared counters
+      topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
+      ia.zero_rows = rc;
+    }
+    e = run_indexer(ia, fp8, stream);
+    if (e != hipSuccess) break;
+    e = run_topk(ta, stream);
+  }
+  return e;
+}
+
 dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t H, int32_t topk, float sm_scale,
                         const void* index_q, dsa_dtype index_dtype, const float* index_q_scale,
                         const void* index_w, dsa_dtype index_w_dtype, const void* index_k,
@@ -290,69 +363,14 @@ dsa_status forward_impl(const dsa_geom* geom, const dsa_pages* pages, int32_t H,
   if (ws_bytes < need || !ws || !aligned(ws, kAlign)) return DSA_ERR_WORKSPACE;
   char* wsb = static_cast<char*>(ws);
   if (!idx_out) idx_out = reinterpret_cast<int32_t*>(wsb + p.total);  // selection kept in the workspace
-  if (keep_all) {
-    // "详解DSA", DSA计算流: a sequence no longer than top-k keeps every
-    // position, so the indexer's work is skipped; the selection is 0 .. pos.
-    TopkArgs ta{};
-    ta.B = geom->B;
-    ta.q_len = geom->q_len;
-    ta.S_max = geom->S_max;
-    ta.seq_lens = geom->seq_lens;
-    ta.row_begin = 0;
-    ta.row_count = T;
-    ta.k = topk;
-    ta.idx = idx_out;
-    const hipError_t e = launch_select_all(ta, stream);
-    if (e != hipSuccess) return DSA_ERR_HIP;
-    return hip_status(mla_launches(geom, pages, H, topk, sm_scale, mla_q, mla_dtype, mla_kv, idx_out, out, lse,
-                                   wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream));
-  }
-  IndexerArgs ia = make_indexer_args(geom, index_q, index_q_scale, index_w, index_w_dtype, index_k, index_k_scale);
-  ia.pages = page_map(pages);
-  hipError_t e = hipSuccess;
-  if (p.streaming) {
-    ia.row_begin = 0;
-    ia.row_count = T;
-    e = launch_indexer_topk_prefill(ia, topk, idx_out, wsb, stream);
-  } else {
-    float* scores = reinterpret_cast<float*>(wsb + p.scores_off);
-    const bool fp8 = index_dtype == DSA_FP8_E4M3FN;
-    for (int r0 = 0; r0 < T && e == hipSuccess; r0 += p.chunk_rows) {
-      const int rc = (T - r0 < p.chunk_rows) ? T - r0 : p.chunk_rows;
-      TopkArgs ta{};
-      ta.B = geom->B;
-      ta.q_len = geom->q_len;
-      ta.S_max = geom->S_max;
-      ta.seq_lens = geom->seq_lens;
-      ta.scores = scores;
-      ta.ld = geom->S_max;
-      ta.row_begin = r0;
-      ta.row_count = rc;
-      ta.k = topk;
-      ta.idx = idx_out + (long long)r0 * topk;
-      ta.ws = wsb + p.topk_off;
-      ta.ws_zeroed = 1;  // the indexer launch below clears the top-k counters
-      if (pages) {       // the top-k also writes the selection as pool rows
-        ta.rows = reinterpret_cast<int32_t*>(wsb + p.rows_off) + (long long)r0 * topk;
-        ta.pages = page_map(pages);
-      }
-      ia.row_begin = r0;
-      ia.row_count = rc;
-      ia.scores = scores;
-      ia.ld = geom->S_max;
-      if (!topk_row_fused(geom->S_max, topk)) {  // the multi-launch top-k counts into cleared counters
-        topk_zero_region(ta.ws, rc, topk, &ia.zero_base, &ia.zero_stride, &ia.zero_words);
-        ia.zero_rows = rc;
-      }
-      e = run_indexer(ia, fp8, stream);
-      if (e != hipSuccess) break;
-      e = run_topk(ta, stream);
-    }
-  }
+  int32_t* rows = reinterpret_cast<int32_t*>(wsb + p.rows_off);
+  const hipError_t e = select_impl(geom, pages, topk, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                                   index_k, index_k_scale, idx_out, wsb, p, rows, stream);
   if (e != hipSuccess) return DSA_ERR_HIP;
+  // the chunked path's top-k already wrote the pool rows of a paged selection
+  const bool rows_ready = !keep_all && !p.streaming;
   return hip_status(mla_launches(geom, pages, H, topk, sm_scale, mla_q, mla_dtype, mla_kv, idx_out, out, lse,
-                                 wsb + p.mla_off, reinterpret_cast<int32_t*>(wsb + p.rows_off), stream,
-                                 /*rows_ready=*/!p.streaming));
+                                 wsb + p.mla_off, rows, stream, rows_ready, /*sel_prefix=*/true));
 }
 
 dsa_status cache_append_impl(const dsa_geom* geom, const dsa_pages* pages, const void* k_new, dsa_dtype k_dtype,
@@ -519,6 +537,30 @@ dsa_status dsa_forward_paged(const dsa_geom* geom, const dsa_pages* pages, int32
                       ws_bytes, stream);
 }
 
+size_t dsa_indexer_topk_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t topk,
+                                       dsa_dtype index_dtype) {
+  if (B < 1 || q_len < 1 || S_max < 1 || topk < 1 || S_max <= topk) return 0;
+  // the selection part of dsa_forward's plan (its size does not depend on H)
+  return plan_forward(B, q_len, S_max, 16, topk, index_dtype, DSA_BF16, false).mla_off;
+}
+
+dsa_status dsa_indexer_topk(const dsa_geom* geom, int32_t topk, const void* index_q, dsa_dtype index_dtype,
+                            const float* index_q_scale, const void* index_w, dsa_dtype index_w_dtype,
+                            const void* index_k, const float* index_k_scale, int32_t* idx_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  const dsa_status st = check_indexer_inputs(geom, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                                             index_k, index_dtype, index_k_scale);
+  if (st != DSA_OK) return st;
+  if (!idx_out || !aligned(idx_out, 4) || topk < 1) return DSA_ERR_INVALID_ARG;
+  const ForwardPlan p = plan_forward(geom->B, geom->q_len, geom->S_max, 16, topk, index_dtype, DSA_BF16, false);
+  const bool keep_all = geom->S_max <= topk;
+  if (!keep_all && !p.streaming && !topk_supported(geom->S_max, topk)) return DSA_ERR_UNSUPPORTED;
+  const size_t need = keep_all ? 0 : p.mla_off;
+  if (ws_bytes < need || (need && (!ws || !aligned(ws, kAlign)))) return DSA_ERR_WORKSPACE;
+  return hip_status(select_impl(geom, nullptr, topk, index_q, index_dtype, index_q_scale, index_w, index_w_dtype,
+                                index_k, index_k_scale, idx_out, static_cast<char*>(ws), p, nullptr, stream));
+}
+
 dsa_status dsa_indexer_quantize(const void* x, dsa_dtype x_dtype, int64_t rows, uint8_t* codes, float* scales,
                                 hipStream_t stream) {
   if (rows < 0) return DSA_ERR_INVALID_ARG;
@@ -650,6 +692,10 @@ size_t dsa_workspace_size(int32_t B, int32_t q_len, int32_t S_max, int32_t H, in
       break;
     case DSA_CALL_INDEXER_KL:
       keep(dsa_indexer_kl_workspace_size(B, q_len, S_max, k));
+      break;
+    case DSA_CALL_INDEXER_TOPK:
+      if (k >= 1)
+        for (dsa_dtype i : idx_dts) keep(dsa_indexer_topk_workspace_size(B, q_len, S_max, k, i));
       break;
     default:
       break;

@@ -283,6 +283,10 @@ struct MlaArgs {
   // sequence b: an entry is valid iff it is >= 0 (the causal bound was applied
   // when the positions were translated).
   int flat;
+  // idx rows are the forward's own selection: ascending, every valid entry
+  // before every -1, exactly min(k, pos + 1) of them, so a row's work can stop
+  // there (a caller's idx may hold -1 anywhere and is read to the end).
+  int sel_prefix;
 };
 
 // Positions idx[t, m] -> pool rows of the paged cache (-1 where the position

@@ -291,7 +291,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_bf16(MlaArgs a, const int32
   const int b = t / a.q_len;
   const int pos = row_pos(a.seq_lens, t, a.q_len, a.S_max);
   const int m0 = split * per_split;
-  const int m1 = min(a.k, m0 + per_split);
+  // with the forward's own selection the valid entries are the first
+  // min(k, pos + 1): a causal row that sees fewer than k keys stops there
+  // instead of gathering and masking -1 tiles
+  const int kv_end = a.sel_prefix ? min(a.k, pos + 1) : a.k;
+  const int m1 = min(kv_end, m0 + per_split);
   // a query that sees no key gathers nothing (its output is zero)
   const int ntiles = (m1 > m0 && pos >= 0) ? (m1 - m0 + kNT - 1) / kNT : 0;
   const bool sh0 = NHB >= SHB * kWaves - 1 || SHB * wave < NHB;                 // this wave has score heads

@@ -113,6 +113,32 @@ def test_forward_workspace_sizes_are_consistent():
     assert lib.dsa_forward_workspace_size(0, 1, 1, 1, 1, 2, 1) == 0
 
 
+def test_indexer_topk_validation_and_workspace():
+    """dsa_indexer_topk: the selection part of dsa_forward's workspace (no
+    attention buffers), zero when every position is selected; a NULL idx_out,
+    bad dtypes and a short workspace are rejected before any launch."""
+    lib = lcl.load()
+    P = ctypes.c_void_p
+    fp8, bf16, f32 = 2, 1, 0
+    dec = lib.dsa_indexer_topk_workspace_size(16, 2, 131072, 2048, fp8)
+    assert 32 * 131072 * 4 <= dec < lib.dsa_forward_workspace_size(16, 2, 131072, 128, 2048, fp8, bf16)
+    pre = lib.dsa_indexer_topk_workspace_size(1, 65536, 65536, 2048, fp8)
+    assert 0 < pre < 65536 * 65536 * 4 // 4           # streamed: never T x S
+    assert lib.dsa_indexer_topk_workspace_size(1, 8, 2048, 2048, fp8) == 0    # S_max <= topk: keep all
+    assert lib.dsa_workspace_size(16, 2, 131072, 128, 2048, lcl.CALL_INDEXER_TOPK) == max(
+        dec, lib.dsa_indexer_topk_workspace_size(16, 2, 131072, 2048, f32))
+    g = _geom(B=1, q_len=1, S=5000)
+    args = (P(FAKE), fp8, None, P(FAKE), bf16, P(FAKE), None)
+    assert lib.dsa_indexer_topk(ctypes.byref(g), 256, *args, None, P(FAKE), 1 << 30, None) == 1   # idx_out NULL
+    assert lib.dsa_indexer_topk(ctypes.byref(g), 0, *args, P(FAKE), P(FAKE), 1 << 30, None) == 1  # topk < 1
+    assert lib.dsa_indexer_topk(ctypes.byref(g), 256, P(FAKE), fp8, None, P(FAKE), bf16, P(FAKE), None,
+                                P(FAKE), P(FAKE), 16, None) == 3                                  # workspace short
+    assert lib.dsa_indexer_topk(ctypes.byref(g), 256, P(FAKE), fp8, None, P(FAKE), bf16, P(FAKE), None,
+                                P(FAKE), None, 1 << 30, None) == 3                                # workspace NULL
+    assert lib.dsa_indexer_topk(ctypes.byref(g), 256, P(FAKE), f32, None, P(FAKE), bf16, P(FAKE), None,
+                                P(FAKE), P(FAKE), 1 << 30, None) == 2                             # f32 q, bf16 w
+
+
 def test_quantize_and_cache_append_validation():
     lib = lcl.load()
     P = ctypes.c_void_p

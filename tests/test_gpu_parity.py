@@ -209,7 +209,9 @@ def test_forward(dsa_gpu, case):
     g = up.geom(dsa_gpu)
     idx, out, lse = dsa_gpu.forward(g, k, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
                                     index_k_scale=up.d_ks)
+    sel = dsa_gpu.indexer_topk(g, k, up.d_qi, up.d_w, up.d_ki, index_k_scale=up.d_ks)
     torch.cuda.synchronize()
+    assert torch.equal(sel, idx), "dsa_indexer_topk differs from dsa_forward's selection"
     gi = idx.cpu().numpy()
     ref = up.oracle_scores()
     pos = wl.positions()
@@ -244,8 +246,10 @@ def test_full_decode(dsa_gpu, name):
     g = up.geom(dsa_gpu)
     idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
                                     index_k_scale=up.d_ks)
+    sel = dsa_gpu.indexer_topk(g, wl.topk, up.d_qi, up.d_w, up.d_ki, index_k_scale=up.d_ks)
     sc = dsa_gpu.indexer_scores(g, up.d_qi, up.d_w, up.d_ki, k_scale=up.d_ks)
     torch.cuda.synchronize()
+    assert torch.equal(sel, idx), "dsa_indexer_topk differs from dsa_forward's selection"
     ref = up.oracle_scores()
     pos = wl.positions()
     got = sc.cpu().numpy()
@@ -288,7 +292,9 @@ def test_full_prefill8k_planted(dsa_gpu):
     g = up.geom(dsa_gpu)
     idx, out, lse = dsa_gpu.forward(g, wl.topk, wl.sm_scale, up.d_qi, up.d_w, up.d_ki, up.d_qm, up.d_kv,
                                     index_k_scale=up.d_ks)
+    sel = dsa_gpu.indexer_topk(g, wl.topk, up.d_qi, up.d_w, up.d_ki, index_k_scale=up.d_ks)
     torch.cuda.synchronize()
+    assert torch.equal(sel, idx), "dsa_indexer_topk differs from dsa_forward's selection"
     gi = idx.cpu().numpy()
     for t in wl.planted_rows:
         assert np.array_equal(gi[t], wl.planted_set), f"planted row {t} lost its planted set"
