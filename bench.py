@@ -429,16 +429,22 @@ def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, 
 
     mla_ws = torch.empty(max(lcl.sparse_mla_workspace_size(B, q_len, H, k, lcl.BF16), 256), dtype=torch.uint8,
                          device=dev)
+    sel = torch.empty_like(idx)
+    sel_ws = torch.empty(max(lcl.indexer_topk_workspace_size(B, q_len, S, k, lcl.FP8_E4M3FN), 256),
+                         dtype=torch.uint8, device=dev)
 
     def mla():
         lcl.sparse_mla(geom, qm, kv, idx, sm, out=out, ws=mla_ws, want_lse=False)
 
+    def select():
+        lcl.indexer_topk(geom, k, qi, w, ki, index_k_scale=ks, idx=sel, ws=sel_ws)
+
     for _ in range(2):
         evict()
         fwd()
-    ts, tm = [], []
+    ts, tm, tsel = [], [], []
     for _ in range(steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         evict()
         e[0].record(stream)
         fwd()
@@ -447,11 +453,17 @@ def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, 
         e[2].record(stream)
         mla()
         e[3].record(stream)
+        evict()
+        e[4].record(stream)
+        select()
+        e[5].record(stream)
         torch.cuda.synchronize()
         ts.append(e[0].elapsed_time(e[1]))
         tm.append(e[2].elapsed_time(e[3]))
+        tsel.append(e[4].elapsed_time(e[5]))
     ms = sum(ts) / len(ts)
     mla_ms = sum(tm) / len(tm)
+    sel_ms = sum(tsel) / len(tsel)
     rate = T / (ms * 1e-3)
     # roofline of the whole step: decode shapes against the HBM floor of the
     # algorithmic bytes, prefill shapes against the MFMA floor of the
@@ -469,13 +481,17 @@ def bench_forward_config(lcl, torch, dev, stream, evict, label, B, q_len, S, k, 
         pairs = B * q_len * (q_len + 1) // 2
         idx_flop, mla_flop = pairs * 64 * 128 * 2, sel * H * (576 + 512) * 2
         floor_ms = idx_flop / (FP8_PEAK_TFLOPS * 1e9) + mla_flop / (BF16_PEAK_TFLOPS * 1e9)
-        i_ms = max(ms - mla_ms, 1e-6)
+        # indexer + top-k timed as its own call (dsa_indexer_topk, the same
+        # launches as inside the forward); the forward's attention is the rest
+        i_ms = sel_ms
+        a_ms = max(ms - i_ms, 1e-6)
         roof = {"bound": "mfma", "indexer_tflop": round(idx_flop / 1e12, 4), "sparse_mla_tflop": round(mla_flop / 1e12, 4),
                 "floor_ms": round(floor_ms, 4), "frac": round(floor_ms / ms, 4),
                 "indexer_topk_ms": round(i_ms, 3),
                 "indexer_fp8_mfma_frac": round(idx_flop / (i_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
-                "sparse_mla_ms": round(mla_ms, 3),
-                "sparse_mla_bf16_mfma_frac": round(mla_flop / (mla_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                "sparse_mla_ms": round(a_ms, 3),
+                "sparse_mla_bf16_mfma_frac": round(mla_flop / (a_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "sparse_mla_standalone_ms": round(mla_ms, 3)}
     log(f"{label}: {ms * 1e3:.1f} us/step -> {rate:,.0f} {unit}; roofline frac {roof['frac']:.3f} ({roof['bound']})")
     del qi, ki, ks, w, qm, kv, idx, out, ws, mla_ws
     torch.cuda.empty_cache()
@@ -631,25 +647,38 @@ def bench_prefill(args, lcl, torch, np, dev, stream, evict):
     ws = torch.empty(lcl.forward_workspace_size(1, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16), dtype=torch.uint8,
                      device=dev)
     mla_ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    sel = torch.empty_like(idx)
+    sel_ws = torch.empty(max(lcl.indexer_topk_workspace_size(1, L, L, k, lcl.FP8_E4M3FN), 256), dtype=torch.uint8,
+                         device=dev)
     sm = 1.0 / math.sqrt(192.0)
-    fwd_ms, mla_ms = [], []
+    fwd_ms, mla_ms, sel_ms = [], [], []
     n = args.prefill_steps
     for i in range(1 + n):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         evict()
         e[0].record(stream)
         lcl.forward(geom, k, sm, qi, w, ki, qm, kv, index_k_scale=ks, idx=idx, out=out, ws=ws, want_lse=False)
         e[1].record(stream)
         lcl.sparse_mla(geom, qm, kv, idx, sm, out=out, ws=mla_ws, want_lse=False)
         e[2].record(stream)
+        evict()
+        e[3].record(stream)
+        lcl.indexer_topk(geom, k, qi, w, ki, index_k_scale=ks, idx=sel, ws=sel_ws)
+        e[4].record(stream)
         torch.cuda.synchronize()
         if i >= 1:
             fwd_ms.append(e[0].elapsed_time(e[1]))
             mla_ms.append(e[1].elapsed_time(e[2]))
-        log(f"prefill step {i}: forward {e[0].elapsed_time(e[1]):.2f} ms, sparse MLA alone {e[1].elapsed_time(e[2]):.2f} ms")
+            sel_ms.append(e[3].elapsed_time(e[4]))
+        log(f"prefill step {i}: forward {e[0].elapsed_time(e[1]):.2f} ms, indexer + top-k alone "
+            f"{e[3].elapsed_time(e[4]):.2f} ms, sparse MLA alone {e[1].elapsed_time(e[2]):.2f} ms")
+    del sel, sel_ws
     f_ms = sum(fwd_ms) / len(fwd_ms)
-    m_ms = sum(mla_ms) / len(mla_ms)
-    i_ms = max(f_ms - m_ms, 1e-6)
+    s_ms = sum(mla_ms) / len(mla_ms)   # the standalone attention call (reads every idx entry)
+    # indexer + top-k timed as its own call (dsa_indexer_topk, the same launches
+    # as inside the forward); the forward's attention is the rest
+    i_ms = sum(sel_ms) / len(sel_ms)
+    m_ms = max(f_ms - i_ms, 1e-6)
     # the same prefill on 64-token pages (scattered seeded table): it streams too
     from synth import make_block_table
     P = 64
@@ -683,13 +712,15 @@ def bench_prefill(args, lcl, torch, np, dev, stream, evict):
     mla_tflops = sel_rows * H * (576 + 512) * 2 / (m_ms * 1e-3) / 1e12
     log(f"prefill: {L / (f_ms * 1e-3):,.0f} tokens/s; indexer+top-k {i_ms:.2f} ms = {idx_tflops:.0f} TFLOP/s "
         f"({idx_tflops / FP8_PEAK_TFLOPS:.1%} fp8 peak); sparse MLA {m_ms:.2f} ms = {mla_tflops:.0f} TFLOP/s "
-        f"({mla_tflops / BF16_PEAK_TFLOPS:.1%} bf16 peak)")
+        f"({mla_tflops / BF16_PEAK_TFLOPS:.1%} bf16 peak; the standalone call, which reads every idx entry, "
+        f"{s_ms:.2f} ms)")
     res = {"workload": "prefill64k: 1 x 65536 causal, indexer fp8 64x128, top-k 2048, 128-head MQA-MLA bf16",
            "tokens_per_s": round(L / (f_ms * 1e-3), 1), "ms_per_step": round(f_ms, 3), "steps": n,
            "indexer_topk_ms": round(i_ms, 3), "indexer_tflops": round(idx_tflops, 1),
            "indexer_fp8_mfma_frac": round(idx_tflops / FP8_PEAK_TFLOPS, 4),
            "sparse_mla_ms": round(m_ms, 3), "sparse_mla_tflops": round(mla_tflops, 1),
            "sparse_mla_bf16_mfma_frac": round(mla_tflops / BF16_PEAK_TFLOPS, 4),
+           "sparse_mla_standalone_ms": round(s_ms, 3),
            "paged_64_token_pages": {"ms_per_step": round(p_ms, 3), "tokens_per_s": round(L / (p_ms * 1e-3), 1),
                                     "vs_contiguous": round(p_ms / f_ms, 4)},
            "workspace_bytes": lcl.forward_workspace_size(1, L, L, H, k, lcl.FP8_E4M3FN, lcl.BF16),
