@@ -140,34 +140,51 @@ def test_topk_threshold_bin_regimes(dsa_gpu):
     bin (4096 < candidates <= 2k + 4096: twelve slots) whose next 10 bits are
     resolved by the second histogram with ties at the k-th score, a bin
     whose next 10 bits hold exactly the remaining count (taken whole), and an
-    overflowing bin (the selection falls back to the score row); exact
+    overflowing bin (the selection falls back to the score row).  Further
+    rows: 3000 distinct top scores on odd positions only, candidates on both
+    sides of zero (the k-th score negative), and infinite scores.  Exact
     against the oracle's rule."""
     _say("[topk] 128K rows: threshold-bin regimes of the final selection")
+    S_max = 131076                                       # every row holds 131072 valid scores
     rng = np.random.default_rng(21)
     S, k = 131072, 2048
-    B = 4
-    scores = rng.uniform(-1.0, 0.5, (B, S)).astype(np.float32)
+    B = 7
+    scores = np.full((B, S_max), 1e30, np.float32)     # columns past S are never read
+    scores[:, :S] = rng.uniform(-1.0, 0.5, (B, S)).astype(np.float32)
     # row 0: a plain spread, few candidates in the threshold bin
-    scores[0] = rng.standard_normal(S).astype(np.float32)
-    # row 1: 1500 clear winners, then 5000 scores inside one 12-bit bin
-    # [1, 1.125) drawn from 640 values (ties at the k-th score)
+    scores[0, :S] = rng.standard_normal(S).astype(np.float32)
+    # row 1: 1500 clear winners, then 5000 scores inside [1, 1.125) drawn
+    # from 640 values (ties at the k-th score)
     p1 = rng.permutation(S)
     scores[1, p1[:1500]] = rng.uniform(100.0, 200.0, 1500)
     scores[1, p1[1500:6500]] = (1.0 + rng.integers(0, 640, 5000) / 8192.0).astype(np.float32)
-    # row 2: 2000 winners, then a bin whose top 10-bit digit holds exactly 48 scores
+    # row 2: 2000 winners, then a digit holding exactly 48 scores
     p2 = rng.permutation(S)
     scores[2, p2[:2000]] = rng.uniform(100.0, 200.0, 2000)
     scores[2, p2[2000:2048]] = np.float32(1.0 + 1023.0 / 8192.0)       # the highest digit of [1, 1.125)
     scores[2, p2[2048:5000]] = (1.0 + rng.integers(0, 1000, 2952) / 8192.0).astype(np.float32)
-    # row 3: 9000 scores in one bin above everything else (more than 2k + 4096)
+    # row 3: 9000 scores in one narrow range above everything else
     p3 = rng.permutation(S)
     scores[3, p3[:9000]] = (1.0 + rng.integers(0, 1024, 9000) / 8192.0).astype(np.float32)
+    # row 4: 3000 distinct top scores at odd positions only (the range
+    # sample reads every 128th position)
+    odd = rng.permutation(np.arange(1, S, 2))[:3000]
+    scores[4, :S] = rng.uniform(-1.0, 0.0, S).astype(np.float32)
+    scores[4, odd] = rng.uniform(10.0, 20.0, 3000).astype(np.float32)
+    # row 5: only 1000 positive scores, so the top-k reaches into the negatives
+    scores[5, :S] = -rng.uniform(1e-3, 5.0, S).astype(np.float32)
+    scores[5, rng.permutation(S)[:1000]] = rng.uniform(1e-3, 5.0, 1000).astype(np.float32)
+    # row 6: 40 +inf, 3000 -inf, 10 equal largest finite scores
+    p6 = rng.permutation(S)
+    scores[6, p6[:40]] = np.inf
+    scores[6, p6[40:3040]] = -np.inf
+    scores[6, p6[3040:3050]] = 3.0e38
     seq = np.full(B, S, np.int32)
     d_seq = torch.from_numpy(seq).cuda()
-    g = dsa_gpu.make_geom(B, 1, S, d_seq)
+    g = dsa_gpu.make_geom(B, 1, S_max, d_seq)
     idx = dsa_gpu.topk(g, torch.from_numpy(scores).cuda(), k).cpu().numpy()
     for r in range(B):
-        want, _ = topk_select(scores[r].astype(np.float64), S - 1, k)
+        want, _ = topk_select(scores[r, :S].astype(np.float64), S - 1, k)
         assert np.array_equal(idx[r], want), f"row {r}"
 
 
