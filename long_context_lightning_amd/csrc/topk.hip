@@ -509,8 +509,8 @@ __global__ __launch_bounds__(kFinThreads) void k_topk_final(TopkArgs a) {
 // has just written (L2 / last-level cache).
 // Longest row sent here.  Longer rows go to several blocks per row: at
 // 131072 scores one block takes 47 us against 33 us for the multi-launch
-// path, its LDS histogram atomics (scores crowd into a few bins) being
-// spread over one CU instead of sixteen.
+// path: the per-score work of its two passes runs on one CU instead of
+// sixteen (bins that spread the scores evenly were slower still).
 constexpr int kRowMaxS = 32768;
 constexpr int kRowMaxK = 2048;
 constexpr int kRowCap = 2 * kRowMaxK + 4096;  // cap_for(kRowMaxK)
