@@ -5,7 +5,9 @@
 // merging into the final top-k, and no full L x L score matrix written to
 // HBM.  This kernel does exactly that on gfx950:
 //
-//  * A block owns 16 consecutive query rows of one sequence (two per wave)
+//  * A block owns 8 consecutive query rows of one sequence (two per wave,
+//    one wave per SIMD; two blocks share a CU, so one block's barrier waits
+//    and list compactions overlap the other's MFMAs)
 //    and walks the causal key range [0, max_pos] in 64-key tiles copied
 //    straight from global memory into LDS one tile ahead (double buffered;
 //    XOR-swizzled 16-byte chunks so the MFMA B-operand reads of consecutive
@@ -34,16 +36,20 @@ namespace dsa {
 
 namespace {
 
-constexpr int kRows = 16;         // query rows per block
-constexpr int kWaves = 8;         // two waves per SIMD
+constexpr int kRows = 8;          // query rows per block
+constexpr int kWaves = 4;         // one per SIMD; two blocks share a CU
 constexpr int kRowsPerWave = kRows / kWaves;
 constexpr int kThreads = kWaves * 64;
 constexpr int kNK = 64;           // keys per tile
 constexpr int kMaxK = 4096;
 
+// Candidate list capacity: k + max(k, 1024), and no more than the LDS
+// staging area of a compaction when k leaves room for it (k = 2048: 3968).
+constexpr int kLdsList = 3968;    // words of one wave's staged list keys
 __host__ __device__ inline int cand_cap(int k) {
   int extra = k > 1024 ? k : 1024;
-  return (k + extra + 63) / 64 * 64;
+  const int cap = (k + extra + 63) / 64 * 64;
+  return (cap > kLdsList && k + 1024 <= kLdsList) ? kLdsList : cap;
 }
 
 // Wait until this wave's vector-memory operations (loads, stores, global ->
@@ -319,7 +325,6 @@ __device__ uint32_t wave_trim(uint32_t* ekey, uint32_t* eidx, int& n, int want, 
 // floor (no dropped key reaches it, so later keys equal to it still lose).
 // FINAL: the kept positions go to pout[0..want), -1 padded, instead of back
 // into the list (a list of at most `want` entries is copied out as it is).
-constexpr int kLdsList = 4096;
 template <bool FINAL>
 __device__ uint32_t wave_compact_lds(uint32_t* ekey, uint32_t* eidx, int& n, int want, int cap, uint32_t* hist,
                                      uint32_t* lk, int32_t* pout) {
@@ -332,10 +337,11 @@ __device__ uint32_t wave_compact_lds(uint32_t* ekey, uint32_t* eidx, int& n, int
   const bool select = nn > want;
   uint32_t tau = 0u, rem = (uint32_t)want;
   if (select) {
-    // Lane l copies words 256b + 4l .. 256b + 4l + 3 of 1 KB block b.
+    // Lane l copies words 256b + 4l .. 256b + 4l + 3 of 1 KB block b, for
+    // the words that hold entries (nn <= cap <= kLdsList, a multiple of 4).
     const int nblk = (nn + 255) / 256;
     for (int b = 0; b < nblk; ++b)
-      dma16_lds(ekey, 4u * (uint32_t)min(256 * b + 4 * lane, cap - 4), lk + 256 * b);
+      if (256 * b + 4 * lane < nn) dma16_lds(ekey, 4u * (uint32_t)min(256 * b + 4 * lane, cap - 4), lk + 256 * b);
     __builtin_amdgcn_s_waitcnt(0);
     wave_sync_mem();
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
@@ -451,14 +457,17 @@ __device__ uint32_t wave_compact_lds(uint32_t* ekey, uint32_t* eidx, int& n, int
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
+__global__ __launch_bounds__(kThreads, 2) void k_prefill(IndexerArgs a, int k, int32_t* idx_out, void* ws, int cap) {
   constexpr int R = kRowsPerWave;
   // K tiles: 128-byte rows, the 16-byte chunk ch of key j at slot ch ^ (j & 7)
   // (the MFMA operand reads of 8 consecutive keys then hit distinct banks).
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2][kNK * kDI];
   __shared__ float ksc[2][kNK];
-  __shared__ uint32_t hist[kWaves][256];  // per-wave compaction histograms
   __shared__ __attribute__((aligned(16))) uint32_t lkeys[kWaves][kLdsList];  // per-wave staged list keys
+  // Two blocks share a CU's LDS (80 KB each): a compaction's per-wave
+  // 256-word histograms live in the key buffer of the tile just consumed.
+  static_assert(kWaves * 256 * 4 <= kNK * kDI, "compaction histograms fit one key buffer");
+  auto hist_of = [&](int buf) { return reinterpret_cast<uint32_t*>(&ktile[buf][0]) + 256 * (threadIdx.x >> 6); };
   __shared__ int need_compact;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -540,13 +549,15 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   }
 
   // Key tiles are copied straight from global memory into LDS, one tile
-  // ahead: wave w moves keys 8w..8w+7 of a tile (lane l: key 8w + l/8, slot
-  // l%8); wave 0 also moves the tile's 64 k-scales.  Keys past the last
-  // row's position read that position's row (their scores are masked).
+  // ahead: in copy j (of kNK / (8 kWaves)) wave w moves keys 8(kWaves j + w)
+  // .. +7 of a tile (lane l: key + l/8, slot l%8); wave 0 also moves the
+  // tile's 64 k-scales.  Keys past the last row's position read that
+  // position's row (their scores are masked).
   const uint8_t* kb8 = static_cast<const uint8_t*>(a.k) + (PAGED ? 0 : (size_t)b * a.S_max * kDI);
   const float* ksb = a.k_scale ? a.k_scale + (PAGED ? 0 : (size_t)b * a.S_max) : nullptr;
   const int ntiles = (maxpos + kNK) / kNK;
-  static_assert(kNK == 8 * kWaves, "one 16-byte copy per lane per tile");
+  constexpr int kCopies = kNK / (8 * kWaves);
+  static_assert(kCopies * 8 * kWaves == kNK, "whole 16-byte copies per lane per tile");
   // Paged caches: a page holds a power of two >= 64 tokens, so a 64-key
   // tile lies inside one page.  Lane i holds the id of page 64*pbatch + i of
   // this sequence (64 pages per batch, refilled when the tiles move past
@@ -569,10 +580,14 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
   };
   auto issue = [&](int ti, int buf) {
     const long long row0 = tile_rows(ti);  // keys ti*kNK .. +63 are rows row0 .. +63
-    const int key = ti * kNK + 8 * wave + (lane >> 3);
-    const int kc = min(key, maxpos) - ti * kNK;
-    const uint32_t chunk = (uint32_t)((lane & 7) ^ (key & 7));
-    dma16_lds(kb8 + row0 * kDI, (uint32_t)kc * kDI + 16u * chunk, &ktile[buf][8 * wave * kDI]);
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      const int kb0 = 8 * (kWaves * j + wave);  // first key of this copy within the tile
+      const int key = ti * kNK + kb0 + (lane >> 3);
+      const int kc = min(key, maxpos) - ti * kNK;
+      const uint32_t chunk = (uint32_t)((lane & 7) ^ (key & 7));
+      dma16_lds(kb8 + row0 * kDI, (uint32_t)kc * kDI + 16u * chunk, &ktile[buf][kb0 * kDI]);
+    }
     if (wave == 0 && ksb) dma4_lds(ksb + row0, 4u * (uint32_t)(min(ti * kNK + lane, maxpos) - ti * kNK), &ksc[buf][0]);
   };
 
@@ -674,10 +689,10 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
         if (n[rr] > trigger) {
           uint32_t tau;
           if (cap <= kLdsList) {
-            tau = wave_compact_lds<false>(ekey[rr], eidx[rr], n[rr], k, cap, hist[wave], lkeys[wave], nullptr);
+            tau = wave_compact_lds<false>(ekey[rr], eidx[rr], n[rr], k, cap, hist_of(buf), lkeys[wave], nullptr);
           } else {
-            tau = wave_trim(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
-            if (n[rr] > trigger) tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+            tau = wave_trim(ekey[rr], eidx[rr], n[rr], k, hist_of(buf));
+            if (n[rr] > trigger) tau = wave_compact(ekey[rr], eidx[rr], n[rr], k, hist_of(buf));
           }
           theta[rr] = max(theta[rr], tau);
         }
@@ -702,9 +717,9 @@ __global__ __launch_bounds__(kThreads) void k_prefill(IndexerArgs a, int k, int3
       continue;
     }
     if (cap <= kLdsList) {
-      wave_compact_lds<true>(ekey[rr], eidx[rr], n[rr], k, cap, hist[wave], lkeys[wave], out);
+      wave_compact_lds<true>(ekey[rr], eidx[rr], n[rr], k, cap, hist_of(0), lkeys[wave], out);
     } else {
-      wave_compact(ekey[rr], eidx[rr], n[rr], k, hist[wave]);
+      wave_compact(ekey[rr], eidx[rr], n[rr], k, hist_of(0));
       for (int j = lane; j < k; j += 64) out[j] = (j < n[rr]) ? (int32_t)eidx[rr][j] : -1;
     }
   }
