@@ -213,6 +213,10 @@ FWD_CASES = [
     ("fwd_prefill_stream", 1, 1500, [1500], 1500, 256, 16, "normal"),
     ("fwd_prefill_stream_b2", 2, 200, [2600, 300], 2600, 128, 16, "normal"),
     ("fwd_prefill_stream_b5", 5, 96, [700, 300, 1200, 96, 2000], 2000, 256, 16, "normal"),  # rotated sequence order
+    # streamed lists of capacity 8192 (k = 4096): compactions on the list in global memory
+    ("fwd_prefill_stream_k4096", 1, 96, [9000], 9000, 4096, 16, "normal"),
+    # k = 2900: the list capacity held at the 3968-word LDS staging area (1068 entries of headroom)
+    ("fwd_prefill_stream_k2900", 1, 128, [7000], 7000, 2900, 16, "normal"),
     ("fwd_keep_all", 2, 70, [300, 100], 300, 512, 16, "normal"),   # S_max <= topk: indexer bypassed
 ]
 
