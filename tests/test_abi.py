@@ -113,6 +113,18 @@ def test_forward_workspace_sizes_are_consistent():
     assert lib.dsa_forward_workspace_size(0, 1, 1, 1, 1, 2, 1) == 0
 
 
+def test_streamed_prefill_workspace_is_the_candidate_lists():
+    """A streamed prefill selection (fp8, q_len >= 64) needs exactly the
+    candidate lists: T rows x (keys, positions) x cap words, cap = k +
+    max(k, 1024) rounded up to 64 and held at the 3968-word LDS staging area
+    of a compaction wherever k + 1024 still fits it."""
+    lib = lcl.load()
+    T = 4096
+    for k, cap in ((64, 1088), (1024, 2048), (1500, 3008), (2048, 3968), (2900, 3968), (3000, 6016),
+                   (4096, 8192)):
+        assert lib.dsa_indexer_topk_workspace_size(1, T, 8192, k, 2) == T * 2 * cap * 4, f"k={k}"
+
+
 def test_indexer_topk_validation_and_workspace():
     """dsa_indexer_topk: the selection part of dsa_forward's workspace (no
     attention buffers), zero when every position is selected; a NULL idx_out,
